@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN recurrence library on one MI355X.
+
+Headline workload: batched decode, GDA, B=64 sequences, H=16 heads,
+d_k=d_v=128, one token per sequence, bf16 q/k/v, fp32 gates and state
+(state [64,16,128,128] fp32 = 64 MiB, read and written in place).
+
+A step is one call of gdn_forward over the whole batch.  The timed region
+holds exactly --steps steps between two stream synchronisations; inputs are
+resident in HBM before it starts.  To measure HBM rather than the 256 MB
+Infinity Cache, the steps rotate over enough independent input/state sets to
+span >= 1 GiB.
+
+Printed: ONE JSON line with the throughput (tokens/s), the roofline of the
+dominant kernel (algorithmic bytes per launch / mean launch time from HIP
+events on the launch stream, against 8 TB/s), the other workloads of the
+path (speculative verify + rollback, KDA verify + rollback, chunked
+prefill), and the float64 CPU oracle timed on a bounded sample on the host
+cores as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+ROTATE_BYTES = 1 << 30  # >= 1 GiB of rotating buffers defeats the 256 MB MALL
+
+METRIC = "GDN tokens/s and achieved HBM GB/s (% peak), decode B=64 H=16 d=128"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (minimum bytes the method must move)
+# ----------------------------------------------------------------------------
+def token_bytes(d: int, kda: bool, bf16: bool) -> int:
+    """Per token and head: q, k, v in, o out (fp32), gate(s) and beta."""
+    e = 2 if bf16 else 4
+    gate = 4 * d if kda else 4
+    return 3 * d * e + gate + 4 + 4 * d
+
+
+def recurrent_bytes(B, T, H, d, K, kda, bf16, final=False) -> int:
+    tile = 4 * d * d
+    n_snap = min(T, K - 1) if K > 1 else 0
+    state = tile + (tile if K == 1 else n_snap * tile) + (tile if final else 0)
+    return B * H * (state + T * token_bytes(d, kda, bf16))
+
+
+def recurrent_flops(B, T, H, d) -> int:
+    # per token-head: two d x d reductions and one rank-1 update (3 d^2 FMA)
+    return B * T * H * 7 * d * d
+
+
+def prefill_bytes(B, T, H, d) -> int:
+    return B * T * H * (3 * 2 * d + 8 + 4 * d) + 2 * B * H * 4 * d * d
+
+
+def prefill_flops(B, T, H, d, C=64) -> int:
+    """Dense-tile MFMA work of the chunk form per head-token: 2 (5 C d + 3 d^2)."""
+    return B * T * H * 2 * (5 * C * d + 3 * d * d)
+
+
+# ----------------------------------------------------------------------------
+# GPU timing helpers
+# ----------------------------------------------------------------------------
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+
+    def mark(self, i):
+        self.ev[i].record(self.torch.cuda.current_stream())
+
+    def pair_ms(self, n):
+        return [self.ev[2 * i].elapsed_time(self.ev[2 * i + 1]) for i in range(n)]
+
+
+def run_timed(torch, launches, steps, warmup):
+    """Run `warmup` then `steps` calls (rotating over `launches`).
+
+    Returns (region_ms, per_launch_ms list).
+    """
+    for i in range(warmup):
+        launches[i % len(launches)]()
+    torch.cuda.synchronize()
+    t = Timer(torch, steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(torch.cuda.current_stream())
+    for i in range(steps):
+        t.mark(2 * i)
+        launches[i % len(launches)]()
+        t.mark(2 * i + 1)
+    end.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), t.pair_ms(steps)
+
+
+def stats(ms):
+    a = np.asarray(ms)
+    return dict(mean_us=float(a.mean() * 1e3), median_us=float(np.median(a) * 1e3),
+                p10_us=float(np.percentile(a, 10) * 1e3), p90_us=float(np.percentile(a, 90) * 1e3))
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+def upload_case(torch, case):
+    qdt = torch.bfloat16 if case.qkv_dtype == "bf16" else torch.float32
+    dev = lambda a, dt=None: (torch.from_numpy(np.ascontiguousarray(a)).to(dt) if dt else
+                              torch.from_numpy(np.ascontiguousarray(a))).to("cuda")
+    return dict(q=dev(case.q, qdt), k=dev(case.k, qdt), v=dev(case.v, qdt), g=dev(case.g),
+                beta=dev(case.beta), state=dev(case.state))
+
+
+def raw_forward_call(lib, stream, case, d, state, o, K=None, final=None):
+    """Pre-marshalled ctypes call of gdn_forward / gdn_forward_snapshots (no
+    per-call Python checks inside the timed loop)."""
+    dt = 1 if case.qkv_dtype == "bf16" else 0
+    gate = 1 if case.gate == "kda" else 0
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    args_common = (p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]))
+    if K is None:
+        args = (case.B, case.T, case.H, case.d_k, case.d_v, dt, gate, *args_common, p(state),
+                p(o), stream)
+        fn = lib.gdn_forward
+    else:
+        args = (case.B, case.T, case.H, case.d_k, case.d_v, dt, gate, K, *args_common, p(state),
+                p(final), p(o), stream)
+        fn = lib.gdn_forward_snapshots
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"libgdn status {st}")
+    return call
+
+
+def bench_decode(torch, lib, stream, steps, warmup):
+    import gdn_inputs as gi
+    case = gi.config_case(1)
+    d = upload_case(torch, case)
+    state0 = d["state"][:, :, 0].contiguous()
+    per_set = state0.numel() * 4
+    n_sets = max(2, -(-ROTATE_BYTES // per_set))
+    sets = []
+    for _ in range(n_sets):
+        # every set gets its own copy of all inputs and of the state
+        ds = {k: v.clone() for k, v in d.items() if k != "state"}
+        ds["state"] = state0.clone()
+        ds["o"] = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
+        sets.append(ds)
+    launches = [raw_forward_call(lib, stream, case, s, s["state"], s["o"]) for s in sets]
+    region_ms, per = run_timed(torch, launches, steps, warmup)
+    tokens = case.B * case.T
+    nbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, 1, False, True)
+    st = stats(per)
+    kern_s = st["mean_us"] * 1e-6
+    res = dict(
+        case=case, n_sets=n_sets, region_ms=region_ms,
+        tokens_per_s=tokens * steps / (region_ms * 1e-3),
+        ms_per_step=region_ms / steps,
+        launch=st, bytes=nbytes,
+        achieved_gbs=nbytes / kern_s / 1e9,
+    )
+    del sets
+    return res
+
+
+def bench_verify(torch, lib, stream, cfg, steps, warmup):
+    """Speculative verify (K=4 snapshots, no final state) then rollback."""
+    import gdn_inputs as gi
+    case = gi.config_case(cfg)
+    d = upload_case(torch, case)
+    per_set = d["state"].numel() * 4
+    n_sets = max(2, -(-ROTATE_BYTES // per_set))
+    acc = torch.from_numpy(case.accepted).to("cuda")
+    sets = []
+    for _ in range(n_sets):
+        ds = {k: v.clone() for k, v in d.items()}
+        ds["o"] = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
+        sets.append(ds)
+    fwd = [raw_forward_call(lib, stream, case, s, s["state"], s["o"], K=case.K) for s in sets]
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def rb_call(s):
+        args = (case.B, case.H, case.K, case.d_k, case.d_v, vp(acc), vp(s["state"]), None, stream)
+
+        def call():
+            st = lib.gdn_rollback_select(*args)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+        return call
+    rbs = [rb_call(s) for s in sets]
+    kda = case.gate == "kda"
+    v_ms, v_per = run_timed(torch, fwd, steps, warmup)
+    r_ms, r_per = run_timed(torch, rbs, steps, warmup)
+    # verify + rollback as one serving step
+    both = [lambda f=f, r=r: (f(), r()) for f, r in zip(fwd, rbs)]
+    b_ms, _ = run_timed(torch, both, steps, warmup)
+    vbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, case.K, kda, True)
+    moved = int(np.count_nonzero(case.accepted > 0))
+    rbytes = 2 * moved * case.H * 4 * case.d_k * case.d_v
+    vs, rs = stats(v_per), stats(r_per)
+    tokens = case.B * case.T
+    out = dict(
+        workload=gi.CONFIGS[cfg]["name"],
+        verify=dict(bytes=vbytes, launch=vs, achieved_gbs=vbytes / (vs["mean_us"] * 1e-6) / 1e9,
+                    tokens_per_s=tokens * steps / (v_ms * 1e-3)),
+        rollback=dict(bytes=rbytes, sequences_rolled=moved, launch=rs,
+                      achieved_gbs=rbytes / (rs["mean_us"] * 1e-6) / 1e9),
+        verify_plus_rollback=dict(ms_per_step=b_ms / steps,
+                                  tokens_per_s=tokens * steps / (b_ms * 1e-3)),
+        n_sets=n_sets,
+    )
+    for key in ("verify", "rollback"):
+        out[key]["frac_of_hbm_peak"] = out[key]["achieved_gbs"] / HBM_PEAK_GBS
+    del sets
+    return out
+
+
+def bench_prefill(torch, lib, stream, steps, warmup):
+    import gdn_inputs as gi
+    case = gi.config_case(4)
+    d = upload_case(torch, case)
+    st0 = d["state"][:, :, 0].contiguous()
+    ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (case.B, case.T, case.H, case.d_k, case.d_v, 64, vp(d["q"]), vp(d["k"]), vp(d["v"]),
+            vp(d["g"]), vp(d["beta"]), vp(st0), vp(o), vp(ws), ws_bytes, stream)
+
+    def call():
+        s = lib.gdn_prefill_chunked(*args)
+        if s != 0:
+            raise RuntimeError(f"libgdn status {s}")
+    region_ms, per = run_timed(torch, [call], steps, warmup)
+    s = stats(per)
+    t = s["mean_us"] * 1e-6
+    nb = prefill_bytes(case.B, case.T, case.H, case.d_k)
+    fl = prefill_flops(case.B, case.T, case.H, case.d_k)
+    return dict(
+        workload=gi.CONFIGS[4]["name"], launch=s, bytes=nb, flops=fl,
+        tokens_per_s=case.B * case.T / t,
+        achieved_gbs=nb / t / 1e9, frac_of_hbm_peak=nb / t / 1e9 / HBM_PEAK_GBS,
+        achieved_tflops=fl / t / 1e12, frac_of_bf16_peak=fl / t / 1e12 / BF16_PEAK_TFLOPS,
+        workspace_bytes=int(ws_bytes),
+    )
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host cores
+# ----------------------------------------------------------------------------
+def cpu_baseline(budget_s: float = 10.0):
+    import gdn_inputs as gi
+    import oracle
+    case = gi.config_case(1)
+    args = [case.f64(n) for n in ("q", "k", "v", "g", "beta")]
+    st = case.f64("state")
+    oracle.forward(*args, st)  # load / build
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args, st)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    tokens = case.B * case.T * reps
+    return dict(value=tokens / el, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"full decode workload (B=64 H=16 d=128 T=1, fp64 per-token loop) "
+                       f"repeated {reps}x in {el:.1f} s, OpenMP over (sequence, head)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "all"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the GDN path is "
+              "benchmarked on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrence_net_amd import _binding
+    if not os.path.exists(_binding.library_path()):
+        from linear_attention_recurrence_net_amd import build
+        build.build()
+    lib = _binding.library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    log("device:", torch.cuda.get_device_name(0))
+
+    log("decode ...")
+    dec = bench_decode(torch, lib, stream, args.steps, args.warmup)
+    log(f"decode: {dec['launch']['mean_us']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s")
+    paths = {}
+    if args.only == "all":
+        for cfg in (2, 3):
+            log(f"verify config {cfg} ...")
+            paths[f"verify_rollback_{'gda' if cfg == 2 else 'kda'}"] = bench_verify(
+                torch, lib, stream, cfg, args.steps, args.warmup)
+        log("prefill ...")
+        try:
+            paths["prefill_chunked_gda"] = bench_prefill(torch, lib, stream,
+                                                         max(5, args.steps // 10),
+                                                         max(2, args.warmup // 10))
+        except RuntimeError as e:
+            paths["prefill_chunked_gda"] = {"error": str(e)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+
+    case = dec["case"]
+    line = {
+        "metric": METRIC,
+        "value": dec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode GDA B=64 H=16 d_k=d_v=128 T=1, bf16 q/k/v, fp32 gates/state "
+                        "(state 64 MiB in place)",
+            "B": case.B, "H": case.H, "d_k": case.d_k, "d_v": case.d_v, "T": case.T,
+            "qkv": "bf16", "state": "f32", "rotating_sets": dec["n_sets"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": dec["achieved_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec["achieved_gbs"] / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "gdn::recurrent_kernel<128, GDA, bf16>",
+            "bytes_per_launch": dec["bytes"],
+            "launch_us": dec["launch"],
+        },
+        "cpu_baseline": cpu,
+        "paths": paths,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

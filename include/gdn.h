@@ -1,0 +1,130 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta net (GDN) library.
+ *
+ * The operation (the gated delta rule; the commit-log pages name it as the
+ * GGML_OP_GATED_DELTA_NET recurrence without writing it out -- llama.cpp
+ * commit log, tag b9752, bullet "metal : add Metal backend for
+ * GGML_OP_GATED_DELTA_NET"): per sequence b and head h the state S is a
+ * d_k x d_v float32 matrix (row i = key index, column j = value index).  For
+ * each token t in order:
+ *
+ *   decay    GDA: S <- exp(g_t) S            (one log-gate per head and token)
+ *            KDA: S[i,:] <- exp(g_t[i]) S[i,:]  (one log-gate per key row)
+ *   delta    u = S^T k_t,   w = beta_t (v_t - u),   S <- S + k_t w^T
+ *   readout  o_t = S^T q_t   (the state after this token's update)
+ *
+ * No scale is applied to q; a caller that wants 1/sqrt(d_k) scales q first.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major array
+ *    (last axis contiguous) owned by the caller.  The library keeps no
+ *    global state, never synchronises and launches only on `stream` (a
+ *    hipStream_t passed as void*; NULL means the default stream).
+ *  - Layouts: q, k [B,T,H,d_k]; v, o [B,T,H,d_v]; g [B,T,H] (GDA) or
+ *    [B,T,H,d_k] (KDA); beta [B,T,H]; state [B,H,K,d_k,d_v] (slot 0 = input).
+ *    q/k/v are float32 or bfloat16 (qkv_dtype); g, beta, state and o are
+ *    float32.  g holds LOG-gates (the decay is exp(g)).
+ *  - Head sizes d_k = d_v in {64, 128} (the sizes the pages' fused kernels
+ *    support; other sizes are reported as unsupported, never computed).
+ *  - Empty problems (B, H or T equal to 0) are valid; the pointers of empty
+ *    arrays may then be NULL.
+ *  - All validation happens on the host before any launch.  On an error
+ *    nothing is launched and no output is touched.  A launch failure is
+ *    reported as GDN_ERR_HIP.  Calls are asynchronous.
+ *  - Outputs must not overlap inputs; final_state must not overlap state.
+ *    NaN/Inf inputs propagate; they are not checked.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    GDN_ERR_SHAPE = 2,       /* a size is negative, or K < 1, or chunk < 1      */
+    GDN_ERR_UNSUPPORTED = 3, /* d_k != d_v, d not in {64,128}, bad dtype/gate   */
+    GDN_ERR_WORKSPACE = 4,   /* prefill workspace missing or too small          */
+    GDN_ERR_HIP = 5          /* the HIP runtime reported a launch error         */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype; /* dtype of q, k, v only */
+typedef enum { GDN_GATE_HEAD = 0 /* GDA */, GDN_GATE_KEY = 1 /* KDA */ } gdn_gate;
+
+/*
+ * Decode / multi-token forward with a single state slot, in place.
+ * state [B,H,d_k,d_v] holds S_0 on entry and S_T on return; o [B,T,H,d_v].
+ * Equivalent to gdn_forward_snapshots with K = 1 and final_state = NULL
+ * (same kernel, bit-identical results).  T = 0 leaves the state unchanged.
+ */
+int gdn_forward(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t qkv_dtype,
+                int32_t gate, const void* q, const void* k, const void* v, const float* g,
+                const float* beta, float* state, float* o, void* stream);
+
+/*
+ * Forward with K snapshot slots for speculative verification (koboldcpp
+ * commit log, tag v1.113.1, bullet "metal: add GDN partial rollback": K is
+ * the slot count, the input state is read from slot 0 of the 3-D state
+ * tensor, intermediate states are written to the slots inside the token
+ * loop, K = 1 keeps the single-slot behaviour).
+ * state [B,H,K,d_k,d_v].  Writes:
+ *   K == 1 : slot 0 <- S_T (exactly gdn_forward);
+ *   K  > 1 : slot t <- S_t (the state after the first t tokens) for
+ *            1 <= t <= min(T, K-1); slot 0 and slots above T are untouched;
+ *   final_state [B,H,d_k,d_v] <- S_T when final_state is not NULL.
+ *   o [B,T,H,d_v] for every token.
+ */
+int gdn_forward_snapshots(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t qkv_dtype, int32_t gate, int32_t K, const void* q,
+                          const void* k, const void* v, const float* g, const float* beta,
+                          float* state, float* final_state, float* o, void* stream);
+
+/*
+ * Rollback to the accepted draft length (koboldcpp commit log, tag v1.113.1,
+ * bullets "llama: allow partial seq_rm for GDN models for speculative
+ * decoding" -- roll back up to draft_max by keeping the GDN intermediates --
+ * and "llama-memory-recurrent: clear rs_idx in clear").
+ * accepted: device int32 [B].  For each sequence b, a = accepted[b]:
+ *   1 <= a <= K-1 : slot 0 of every head <- slot a, bit for bit;
+ *   a == 0        : no change;
+ *   a < 0, a >= K : the sequence is left untouched and, when err_flag is not
+ *                   NULL, *err_flag (a device int32 the caller zeroes) is
+ *                   set to 1.
+ * state [B,H,K,d_k,d_v].  Any d_k, d_v >= 1 with d_k*d_v a multiple of 4.
+ */
+int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_v,
+                        const int32_t* accepted, float* state, int32_t* err_flag, void* stream);
+
+/*
+ * Chunked prefill (llama.cpp commit log, tag b9752, bullet "llama : enable
+ * chunked fused GDN path"; the chunk algebra is the WY/UT form of the same
+ * recurrence and gives the same result up to rounding).
+ * GDA only, q/k/v bfloat16, d_k = d_v in {64,128}, chunk = 64, any T >= 0
+ * (a short final chunk behaves as if padded with beta = 0, g = 0, k = q = v = 0).
+ * state [B,H,d_k,d_v] float32 holds S_0 on entry and S_T on return;
+ * o [B,T,H,d_v] float32.  Contractions run on bf16 MFMA with float32
+ * accumulation; the carried state stays float32.
+ * workspace: device memory of at least gdn_prefill_workspace_size(...)
+ * bytes, 256-byte aligned, owned by the caller; its contents on entry are
+ * ignored and on return are unspecified.
+ */
+size_t gdn_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                  int32_t chunk);
+int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                        int32_t chunk, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, float* state, float* o,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gdn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,23 @@
+"""MI355X (gfx950) gated delta net (GDN) recurrence.
+
+A thin Python binding over the C-ABI library ``libgdn.so`` (declared in
+``include/gdn.h``).  Every step of the computation runs in the library's HIP
+kernels; this package only checks torch tensors and passes their device
+pointers and the current HIP stream.  There is no CPU fallback: if the
+library is missing or a tensor is not on the GPU, the call raises.
+
+Entry points (same names as the C ABI):
+  gdn_forward, gdn_forward_snapshots, gdn_rollback_select,
+  gdn_prefill_workspace_size, gdn_prefill_chunked
+"""
+
+from ._binding import (  # noqa: F401
+    GdnError,
+    gdn_forward,
+    gdn_forward_snapshots,
+    gdn_prefill_chunked,
+    gdn_prefill_workspace_size,
+    gdn_rollback_select,
+    library,
+    library_path,
+)

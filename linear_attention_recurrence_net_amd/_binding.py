@@ -1,0 +1,212 @@
+"""ctypes binding of libgdn.so: argument checks and marshalling only."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
+
+EXPORTED = (
+    "gdn_forward",
+    "gdn_forward_snapshots",
+    "gdn_rollback_select",
+    "gdn_prefill_workspace_size",
+    "gdn_prefill_chunked",
+    "gdn_status_str",
+)
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    """A non-zero status returned by libgdn."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m linear_attention_recurrence_net_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.gdn_forward.argtypes = [i32] * 7 + [vp] * 8
+    lib.gdn_forward.restype = ctypes.c_int
+    lib.gdn_forward_snapshots.argtypes = [i32] * 8 + [vp] * 9
+    lib.gdn_forward_snapshots.restype = ctypes.c_int
+    lib.gdn_rollback_select.argtypes = [i32] * 5 + [vp] * 4
+    lib.gdn_rollback_select.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_size.argtypes = [i32] * 6
+    lib.gdn_prefill_workspace_size.restype = sz
+    lib.gdn_prefill_chunked.argtypes = [i32] * 6 + [vp] * 8 + [sz, vp]
+    lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_status_str.argtypes = [ctypes.c_int]
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise GdnError(fn, status, library().gdn_status_str(status).decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dtypes, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(name: str, t: torch.Tensor, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _qkv_gate(q, k, v, g, beta):
+    _dev_tensor("q", q, (torch.float32, torch.bfloat16))
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,d_k]")
+    B, T, H, dk = q.shape
+    _dev_tensor("k", k, (q.dtype,), dev)
+    _dev_tensor("v", v, (q.dtype,), dev)
+    _shape("k", k, (B, T, H, dk))
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("v must be [B,T,H,d_v]")
+    dv = v.shape[3]
+    _dev_tensor("g", g, (torch.float32,), dev)
+    _dev_tensor("beta", beta, (torch.float32,), dev)
+    _shape("beta", beta, (B, T, H))
+    if g.dim() == 3:
+        _shape("g", g, (B, T, H))
+        gate = GDN_GATE_HEAD
+    else:
+        _shape("g", g, (B, T, H, dk))
+        gate = GDN_GATE_KEY
+    dt = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    return B, T, H, dk, dv, dt, gate, dev
+
+
+def gdn_forward(q, k, v, g, beta, state, o=None):
+    """Single-slot forward, state [B,H,d_k,d_v] updated in place; returns o.
+
+    g is [B,T,H] (GDA) or [B,T,H,d_k] (KDA) log-gates.
+    """
+    B, T, H, dk, dv, dt, gate, dev = _qkv_gate(q, k, v, g, beta)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    _shape("state", state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    st = library().gdn_forward(B, T, H, dk, dv, dt, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(state), _ptr(o), _stream_ptr(dev))
+    _check("gdn_forward", st)
+    return o
+
+
+def gdn_forward_snapshots(q, k, v, g, beta, state, final_state=None, o=None):
+    """Forward with K snapshot slots, state [B,H,K,d_k,d_v]; returns o."""
+    B, T, H, dk, dv, dt, gate, dev = _qkv_gate(q, k, v, g, beta)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    if state.dim() != 5:
+        raise ValueError("state must be [B,H,K,d_k,d_v]")
+    K = state.shape[2]
+    _shape("state", state, (B, H, K, dk, dv))
+    if final_state is not None:
+        _dev_tensor("final_state", final_state, (torch.float32,), dev)
+        _shape("final_state", final_state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    st = library().gdn_forward_snapshots(B, T, H, dk, dv, dt, gate, K, _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(g), _ptr(beta), _ptr(state), _ptr(final_state),
+                                         _ptr(o), _stream_ptr(dev))
+    _check("gdn_forward_snapshots", st)
+    return o
+
+
+def gdn_rollback_select(accepted, state, err_flag=None):
+    """Copy slot accepted[b] to slot 0 for every sequence b (in place).
+
+    err_flag: optional device int32 tensor of one element that the caller
+    zeroes; set to 1 when an accepted value is outside 0..K-1.
+    """
+    _dev_tensor("state", state, (torch.float32,), None)
+    dev = state.device
+    if state.dim() != 5:
+        raise ValueError("state must be [B,H,K,d_k,d_v]")
+    B, H, K, dk, dv = state.shape
+    _dev_tensor("accepted", accepted, (torch.int32,), dev)
+    _shape("accepted", accepted, (B,))
+    if err_flag is not None:
+        _dev_tensor("err_flag", err_flag, (torch.int32,), dev)
+        if err_flag.numel() < 1:
+            raise ValueError("err_flag must hold one int32")
+    st = library().gdn_rollback_select(B, H, K, dk, dv, _ptr(accepted), _ptr(state),
+                                       _ptr(err_flag), _stream_ptr(dev))
+    _check("gdn_rollback_select", st)
+
+
+def gdn_prefill_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, chunk: int = 64) -> int:
+    return int(library().gdn_prefill_workspace_size(B, T, H, d_k, d_v, chunk))
+
+
+def gdn_prefill_chunked(q, k, v, g, beta, state, o=None, workspace=None, chunk: int = 64):
+    """Chunked prefill (GDA, bf16 q/k/v), state [B,H,d_k,d_v] in place; returns o.
+
+    workspace: optional uint8 device tensor of at least
+    gdn_prefill_workspace_size(...) bytes; allocated here when omitted.
+    """
+    B, T, H, dk, dv, dt, gate, dev = _qkv_gate(q, k, v, g, beta)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    _shape("state", state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    if gate != GDN_GATE_HEAD:
+        raise GdnError("gdn_prefill_chunked", 3, "chunked prefill supports GDA gates only")
+    need = gdn_prefill_workspace_size(B, T, H, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked(B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
+                                       workspace.numel(), _stream_ptr(dev))
+    _check("gdn_prefill_chunked", st)
+    return o

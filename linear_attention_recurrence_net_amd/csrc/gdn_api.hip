@@ -1,0 +1,137 @@
+// gdn_api.hip -- the extern "C" entry points of gdn.h: host-side validation,
+// kernel selection and launch on the caller's stream.  Nothing here
+// allocates, synchronises or keeps state between calls.
+
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_head(int d_k, int d_v) { return d_k == d_v && (d_k == 64 || d_k == 128); }
+
+int check_launch(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+int validate_recurrent(int B, int T, int H, int d_k, int d_v, int qkv_dtype, int gate, int K,
+                       const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* state, const float* final_state,
+                       const float* o) {
+    if (B < 0 || T < 0 || H < 0 || K < 1) return GDN_ERR_SHAPE;
+    // Empty token arrays (T == 0) and empty batches may come with NULL pointers.
+    const bool tokens = B > 0 && H > 0 && T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
+    if (!supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(state) ||
+        !aligned16(o) || (final_state && !aligned16(final_state)))
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_forward_snapshots(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t qkv_dtype, int32_t gate, int32_t K, const void* q,
+                          const void* k, const void* v, const float* g, const float* beta,
+                          float* state, float* final_state, float* o, void* stream) {
+    int st = validate_recurrent(B, T, H, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                final_state, o);
+    if (st != GDN_OK) return st;
+    if (B == 0 || H == 0) return GDN_OK;
+    // With no token, nothing changes unless a final_state copy is requested.
+    if (T == 0 && final_state == nullptr) return GDN_OK;
+    gdn::RecurrentArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.final_state = final_state;
+    a.o = o;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.K = K;
+    a.d = d_k;
+    a.n_snap = K > 1 ? (T < K - 1 ? T : K - 1) : 0;
+    a.bf16 = qkv_dtype == GDN_BF16;
+    a.kda = gate == GDN_GATE_KEY;
+    return check_launch(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_forward(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t qkv_dtype,
+                int32_t gate, const void* q, const void* k, const void* v, const float* g,
+                const float* beta, float* state, float* o, void* stream) {
+    return gdn_forward_snapshots(B, T, H, d_k, d_v, qkv_dtype, gate, 1, q, k, v, g, beta, state,
+                                 nullptr, o, stream);
+}
+
+int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_v,
+                        const int32_t* accepted, float* state, int32_t* err_flag, void* stream) {
+    if (B < 0 || H < 0 || K < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if (B > 0 && (!accepted || (H > 0 && !state))) return GDN_ERR_NULL;
+    const size_t tile = static_cast<size_t>(d_k) * static_cast<size_t>(d_v);
+    if (tile % 4 != 0 || !aligned16(state)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return GDN_OK;
+    return check_launch(gdn::launch_rollback(B, H, K, tile, accepted, state, err_flag,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                  int32_t chunk) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    return gdn::prefill_workspace_bytes(B, T, H, d_k);
+}
+
+int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                        int32_t chunk, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, float* state, float* o,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || T < 0 || H < 0 || chunk < 1) return GDN_ERR_SHAPE;
+    const bool tokens = B > 0 && H > 0 && T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
+    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
+        return GDN_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) return GDN_OK;
+    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k);
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return GDN_ERR_WORKSPACE;
+    gdn::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.workspace = workspace;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.d = d_k;
+    return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* gdn_status_str(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "invalid size (negative B/T/H, K < 1 or chunk < 1)";
+        case GDN_ERR_UNSUPPORTED:
+            return "unsupported configuration (head size, dtype, gate mode, chunk or alignment)";
+        case GDN_ERR_WORKSPACE: return "prefill workspace missing, misaligned or too small";
+        case GDN_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// gdn_internal.hpp -- launch descriptors shared by the host entry points and
+// the kernel translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct RecurrentArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;        // [B,H,K,d,d]
+    float* final_state;  // [B,H,d,d] or nullptr
+    float* o;            // [B,T,H,d]
+    int B, T, H, K, d;
+    int n_snap;          // snapshot slots written: K > 1 ? min(T, K-1) : 0
+    bool bf16, kda;
+};
+
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
+
+hipError_t launch_rollback(int B, int H, int K, size_t tile_elems, const int32_t* accepted,
+                           float* state, int32_t* err_flag, hipStream_t stream);
+
+struct PrefillArgs {
+    const void* q;  // bf16 [B,T,H,d]
+    const void* k;
+    const void* v;
+    const float* g;     // [B,T,H]
+    const float* beta;  // [B,T,H]
+    float* state;       // [B,H,d,d] in/out
+    float* o;           // [B,T,H,d]
+    void* workspace;
+    int B, T, H, d;
+};
+
+size_t prefill_workspace_bytes(int B, int T, int H, int d);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,61 @@
+// gdn_rollback.hip -- restore the accepted snapshot slot into slot 0.
+//
+// After speculative verification a sequence keeps the state after its
+// accepted tokens (koboldcpp commit log, tag v1.113.1, bullet "llama: allow
+// partial seq_rm for GDN models for speculative decoding").  The snapshot
+// kernel left S_a in slot a, so the rollback is a bitwise copy slot a -> 0
+// for every head of the sequence: a pure streaming copy, bound by HBM.
+//
+// One workgroup of 256 lanes copies one (sequence, head) tile; each lane
+// issues all of its 128-bit loads before its stores.  Workgroups of
+// sequences with a == 0 exit at once.
+
+#include "device_common.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+constexpr int kCopyThreads = 256;
+
+template <int PER_LANE>
+__global__ void __launch_bounds__(kCopyThreads)
+rollback_kernel(const int32_t* __restrict__ accepted, float* __restrict__ state, int H, int K,
+                size_t tile_vec4, int32_t* __restrict__ err_flag) {
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const int a = accepted[b];
+    if (a < 0 || a >= K) {
+        if (h == 0 && threadIdx.x == 0 && err_flag != nullptr) atomicOr(err_flag, 1);
+        return;
+    }
+    if (a == 0) return;
+    float* base = state + static_cast<size_t>(bh) * K * tile_vec4 * 4;
+    const float* src = base + static_cast<size_t>(a) * tile_vec4 * 4;
+    if constexpr (PER_LANE > 0) {
+        // tile_vec4 == PER_LANE * kCopyThreads
+        f32x4 r[PER_LANE];
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) r[i] = ld4_nt(src + 4 * (i * kCopyThreads + threadIdx.x));
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) st4_nt(base + 4 * (i * kCopyThreads + threadIdx.x), r[i]);
+    } else {
+        for (size_t i = threadIdx.x; i < tile_vec4; i += kCopyThreads) st4(base + 4 * i, ld4(src + 4 * i));
+    }
+}
+
+hipError_t launch_rollback(int B, int H, int K, size_t tile_elems, const int32_t* accepted,
+                           float* state, int32_t* err_flag, hipStream_t stream) {
+    const size_t tile_vec4 = tile_elems / 4;
+    dim3 grid(static_cast<unsigned>(B) * static_cast<unsigned>(H));
+    dim3 block(kCopyThreads);
+    if (tile_vec4 == 16 * kCopyThreads)
+        hipLaunchKernelGGL(rollback_kernel<16>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
+    else if (tile_vec4 == 4 * kCopyThreads)
+        hipLaunchKernelGGL(rollback_kernel<4>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
+    else
+        hipLaunchKernelGGL(rollback_kernel<0>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

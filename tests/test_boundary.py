@@ -1,0 +1,134 @@
+"""C-ABI boundary checks that need no GPU.
+
+* libgdn.so loads and exports every function include/gdn.h declares;
+* argument validation happens on the host before any HIP call: NULL
+  pointers, bad sizes, unsupported head sizes / dtypes / gates / chunk
+  sizes, misalignment and a short prefill workspace return their status
+  codes without launching (so these calls are safe without a GPU);
+* the status strings exist for every code;
+* the Python binding refuses CPU tensors (there is no CPU path).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import linear_attention_recurrence_net_amd as gdn
+from linear_attention_recurrence_net_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP = range(6)
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.library_path()):
+        from linear_attention_recurrence_net_amd import build
+        build.build()
+    return gdn.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_binding.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.gdn_status_str(s)
+    assert b"unknown" in lib.gdn_status_str(99)
+
+
+P = ctypes.c_void_p(256)  # a fake, 16-byte aligned "device" pointer: never dereferenced
+N = None
+
+
+def fwd(lib, B=1, T=1, H=1, dk=64, dv=64, dt=1, gate=0, q=P, k=P, v=P, g=P, beta=P, st=P, o=P):
+    return lib.gdn_forward(B, T, H, dk, dv, dt, gate, q, k, v, g, beta, st, o, None)
+
+
+def snap(lib, K=4, fin=N, **kw):
+    a = dict(B=1, T=1, H=1, dk=64, dv=64, dt=1, gate=0, q=P, k=P, v=P, g=P, beta=P, st=P, o=P)
+    a.update(kw)
+    return lib.gdn_forward_snapshots(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["gate"],
+                                     K, a["q"], a["k"], a["v"], a["g"], a["beta"], a["st"], fin,
+                                     a["o"], None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, q=N) == ERR_NULL
+    assert fwd(lib, st=N) == ERR_NULL
+    assert fwd(lib, o=N) == ERR_NULL
+    assert fwd(lib, B=-1) == ERR_SHAPE
+    assert fwd(lib, T=-3) == ERR_SHAPE
+    assert fwd(lib, dk=32, dv=32) == ERR_UNSUP  # head size 32 is not supported
+    assert fwd(lib, dk=64, dv=128) == ERR_UNSUP
+    assert fwd(lib, dk=96, dv=96) == ERR_UNSUP
+    assert fwd(lib, dt=7) == ERR_UNSUP
+    assert fwd(lib, gate=2) == ERR_UNSUP
+    assert fwd(lib, q=ctypes.c_void_p(258)) == ERR_UNSUP  # misaligned
+    # empty problems are valid and launch nothing
+    assert fwd(lib, B=0) == OK
+    assert fwd(lib, H=0) == OK
+    assert fwd(lib, T=0) == OK
+
+
+def test_snapshot_validation(lib):
+    assert snap(lib, K=0) == ERR_SHAPE
+    assert snap(lib, K=-2) == ERR_SHAPE
+    assert snap(lib, K=4, fin=ctypes.c_void_p(264)) == ERR_UNSUP
+    assert snap(lib, K=4, B=0) == OK
+
+
+def test_rollback_validation(lib):
+    rb = lib.gdn_rollback_select
+    assert rb(1, 1, 4, 64, 64, N, P, N, None) == ERR_NULL
+    assert rb(1, 1, 4, 64, 64, P, N, N, None) == ERR_NULL
+    assert rb(1, 1, 0, 64, 64, P, P, N, None) == ERR_SHAPE
+    assert rb(-1, 1, 4, 64, 64, P, P, N, None) == ERR_SHAPE
+    assert rb(1, 1, 4, 3, 3, P, P, N, None) == ERR_UNSUP  # tile not a multiple of 4
+    assert rb(0, 1, 4, 64, 64, P, P, N, None) == OK
+
+
+def test_prefill_validation(lib):
+    ws = lib.gdn_prefill_workspace_size
+    need = ws(1, 8192, 16, 128, 128, 64)
+    assert need > 0
+    assert ws(1, 8192, 16, 128, 128, 32) == 0
+    assert ws(1, 8192, 16, 32, 32, 64) == 0
+    pf = lib.gdn_prefill_chunked
+    big = need
+    assert pf(1, 100, 2, 128, 128, 64, N, P, P, P, P, P, P, P, big, None) == ERR_NULL
+    assert pf(1, 100, 2, 128, 128, 0, P, P, P, P, P, P, P, P, big, None) == ERR_SHAPE
+    assert pf(1, 100, 2, 128, 128, 32, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
+    assert pf(1, 100, 2, 96, 96, 64, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
+    small = ws(1, 100, 2, 128, 128, 64)
+    assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, N, small, None) == ERR_WS
+    assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, P, small - 1, None) == ERR_WS
+    assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, ctypes.c_void_p(272), small, None) == ERR_WS
+    assert pf(1, 0, 2, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == OK
+
+
+def test_workspace_grows_with_tokens(lib):
+    ws = lib.gdn_prefill_workspace_size
+    assert ws(1, 64, 16, 128, 128, 64) <= ws(1, 65, 16, 128, 128, 64) <= ws(1, 8192, 16, 128, 128, 64)
+    assert ws(2, 8192, 16, 128, 128, 64) >= ws(1, 8192, 16, 128, 128, 64)
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    q = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16)
+    g = torch.zeros(1, 1, 1)
+    with pytest.raises(ValueError, match="GPU"):
+        gdn.gdn_forward(q, q, q, g, g, torch.zeros(1, 1, 64, 64))
