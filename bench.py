@@ -6,17 +6,18 @@ d_k=d_v=128, one token per sequence, bf16 q/k/v, fp32 gates and state
 (state [64,16,128,128] fp32 = 64 MiB, read and written in place).
 
 A step is one call of gdn_forward over the whole batch.  The timed region
-holds exactly --steps steps between two stream synchronisations; inputs are
-resident in HBM before it starts.  To measure HBM rather than the 256 MB
+holds exactly --steps steps between two device synchronisations: the steps
+are captured once into a HIP graph (removing Python launch overhead) and one
+replay is timed with HIP events on the stream the kernels run on.  Inputs
+are resident in HBM before it starts.  To measure HBM rather than the 256 MB
 Infinity Cache, the steps rotate over enough independent input/state sets to
 span >= 1 GiB.
 
 Printed: ONE JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel (algorithmic bytes per launch / mean launch time from HIP
-events on the launch stream, against 8 TB/s), the other workloads of the
-path (speculative verify + rollback, KDA verify + rollback, chunked
-prefill), and the float64 CPU oracle timed on a bounded sample on the host
-cores as a baseline.
+dominant kernel (algorithmic bytes per launch / mean launch time, against
+8 TB/s), the other workloads of the path (speculative verify + rollback, KDA
+verify + rollback, chunked prefill), and the float64 CPU oracle timed on a
+bounded sample on the host cores as a baseline.
 """
 
 from __future__ import annotations
@@ -78,46 +79,48 @@ def prefill_flops(B, T, H, d, C=64) -> int:
 # ----------------------------------------------------------------------------
 # GPU timing helpers
 # ----------------------------------------------------------------------------
-class Timer:
-    """HIP events on the stream the kernels are launched on."""
+def run_timed(torch, calls, steps, warmup):
+    """Time exactly `steps` launches (rotating over `calls`).
 
-    def __init__(self, torch, n):
-        self.torch = torch
-        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
-
-    def mark(self, i):
-        self.ev[i].record(self.torch.cuda.current_stream())
-
-    def pair_ms(self, n):
-        return [self.ev[2 * i].elapsed_time(self.ev[2 * i + 1]) for i in range(n)]
-
-
-def run_timed(torch, launches, steps, warmup):
-    """Run `warmup` then `steps` calls (rotating over `launches`).
-
-    Returns (region_ms, per_launch_ms list).
+    Each call takes the HIP stream handle to launch on.  Warmup: `warmup`
+    eager launches, then the `steps` launches are captured once into a HIP
+    graph and the graph is replayed once untimed.  The timed region is one
+    replay of that graph between two HIP events recorded on the stream the
+    kernels run on, bracketed by device synchronisations.  Returns
+    (region_ms, eager_ms_per_step) where the second figure times the same
+    launches issued one by one from Python (launch overhead included).
     """
+    cur = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(cur.cuda_stream)
     for i in range(warmup):
-        launches[i % len(launches)]()
+        calls[i % len(calls)](sp)
     torch.cuda.synchronize()
-    t = Timer(torch, steps)
+    # eager reference timing (host launch overhead included)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_eager = min(steps, 50)
+    e0.record(cur)
+    for i in range(n_eager):
+        calls[i % len(calls)](sp)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / n_eager
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(steps):
+            calls[i % len(calls)](gs)
+    graph.replay()
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    start.record(cur)
+    graph.replay()
+    end.record(cur)
     torch.cuda.synchronize()
-    start.record(torch.cuda.current_stream())
-    for i in range(steps):
-        t.mark(2 * i)
-        launches[i % len(launches)]()
-        t.mark(2 * i + 1)
-    end.record(torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    return start.elapsed_time(end), t.pair_ms(steps)
-
-
-def stats(ms):
-    a = np.asarray(ms)
-    return dict(mean_us=float(a.mean() * 1e3), median_us=float(np.median(a) * 1e3),
-                p10_us=float(np.percentile(a, 10) * 1e3), p90_us=float(np.percentile(a, 90) * 1e3))
+    region_ms = start.elapsed_time(end)
+    del graph
+    return region_ms, eager_ms
 
 
 # ----------------------------------------------------------------------------
@@ -131,7 +134,7 @@ def upload_case(torch, case):
                 beta=dev(case.beta), state=dev(case.state))
 
 
-def raw_forward_call(lib, stream, case, d, state, o, K=None, final=None):
+def raw_forward_call(lib, case, d, state, o, K=None, final=None):
     """Pre-marshalled ctypes call of gdn_forward / gdn_forward_snapshots (no
     per-call Python checks inside the timed loop)."""
     dt = 1 if case.qkv_dtype == "bf16" else 0
@@ -140,130 +143,131 @@ def raw_forward_call(lib, stream, case, d, state, o, K=None, final=None):
     args_common = (p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]))
     if K is None:
         args = (case.B, case.T, case.H, case.d_k, case.d_v, dt, gate, *args_common, p(state),
-                p(o), stream)
+                p(o))
         fn = lib.gdn_forward
     else:
         args = (case.B, case.T, case.H, case.d_k, case.d_v, dt, gate, K, *args_common, p(state),
-                p(final), p(o), stream)
+                p(final), p(o))
         fn = lib.gdn_forward_snapshots
 
-    def call():
-        st = fn(*args)
+    def call(stream):
+        st = fn(*args, stream)
         if st != 0:
             raise RuntimeError(f"libgdn status {st}")
     return call
 
 
-def bench_decode(torch, lib, stream, steps, warmup):
+def _rotating_sets(torch, d, case, with_state_slot0=False):
+    """Independent copies of all inputs and the state, >= 1 GiB in total."""
+    state = d["state"][:, :, 0].contiguous() if with_state_slot0 else d["state"]
+    n_sets = max(2, -(-ROTATE_BYTES // (state.numel() * 4)))
+    sets = []
+    for _ in range(n_sets):
+        ds = {k: v.clone() for k, v in d.items() if k != "state"}
+        ds["state"] = state.clone()
+        ds["o"] = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
+        sets.append(ds)
+    return sets
+
+
+def _timing(region_ms, eager_ms, steps):
+    per = region_ms / steps
+    return dict(ms_per_step=per, us_per_launch=per * 1e3, eager_us_per_launch=eager_ms * 1e3)
+
+
+def bench_decode(torch, lib, steps, warmup):
     import gdn_inputs as gi
     case = gi.config_case(1)
     d = upload_case(torch, case)
-    state0 = d["state"][:, :, 0].contiguous()
-    per_set = state0.numel() * 4
-    n_sets = max(2, -(-ROTATE_BYTES // per_set))
-    sets = []
-    for _ in range(n_sets):
-        # every set gets its own copy of all inputs and of the state
-        ds = {k: v.clone() for k, v in d.items() if k != "state"}
-        ds["state"] = state0.clone()
-        ds["o"] = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
-        sets.append(ds)
-    launches = [raw_forward_call(lib, stream, case, s, s["state"], s["o"]) for s in sets]
-    region_ms, per = run_timed(torch, launches, steps, warmup)
-    tokens = case.B * case.T
+    sets = _rotating_sets(torch, d, case, with_state_slot0=True)
+    calls = [raw_forward_call(lib, case, s, s["state"], s["o"]) for s in sets]
+    region_ms, eager_ms = run_timed(torch, calls, steps, warmup)
     nbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, 1, False, True)
-    st = stats(per)
-    kern_s = st["mean_us"] * 1e-6
-    res = dict(
-        case=case, n_sets=n_sets, region_ms=region_ms,
-        tokens_per_s=tokens * steps / (region_ms * 1e-3),
-        ms_per_step=region_ms / steps,
-        launch=st, bytes=nbytes,
-        achieved_gbs=nbytes / kern_s / 1e9,
-    )
-    del sets
+    t = _timing(region_ms, eager_ms, steps)
+    res = dict(case=case, n_sets=len(sets), region_ms=region_ms,
+               tokens_per_s=case.B * case.T * steps / (region_ms * 1e-3),
+               bytes=nbytes, achieved_gbs=nbytes / (t["us_per_launch"] * 1e-6) / 1e9, **t)
+    del sets, calls
+    torch.cuda.empty_cache()
     return res
 
 
-def bench_verify(torch, lib, stream, cfg, steps, warmup):
-    """Speculative verify (K=4 snapshots, no final state) then rollback."""
+def bench_verify(torch, lib, cfg, steps, warmup):
+    """Speculative verify (K=4 snapshots, no final state), then rollback."""
     import gdn_inputs as gi
     case = gi.config_case(cfg)
     d = upload_case(torch, case)
-    per_set = d["state"].numel() * 4
-    n_sets = max(2, -(-ROTATE_BYTES // per_set))
+    sets = _rotating_sets(torch, d, case)
     acc = torch.from_numpy(case.accepted).to("cuda")
-    sets = []
-    for _ in range(n_sets):
-        ds = {k: v.clone() for k, v in d.items()}
-        ds["o"] = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
-        sets.append(ds)
-    fwd = [raw_forward_call(lib, stream, case, s, s["state"], s["o"], K=case.K) for s in sets]
+    fwd = [raw_forward_call(lib, case, s, s["state"], s["o"], K=case.K) for s in sets]
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
 
     def rb_call(s):
-        args = (case.B, case.H, case.K, case.d_k, case.d_v, vp(acc), vp(s["state"]), None, stream)
+        args = (case.B, case.H, case.K, case.d_k, case.d_v, vp(acc), vp(s["state"]), None)
 
-        def call():
-            st = lib.gdn_rollback_select(*args)
+        def call(stream):
+            st = lib.gdn_rollback_select(*args, stream)
             if st != 0:
                 raise RuntimeError(f"libgdn status {st}")
         return call
     rbs = [rb_call(s) for s in sets]
+
+    def both(f, r):
+        def call(stream):
+            f(stream)
+            r(stream)
+        return call
+    pair = [both(f, r) for f, r in zip(fwd, rbs)]
     kda = case.gate == "kda"
-    v_ms, v_per = run_timed(torch, fwd, steps, warmup)
-    r_ms, r_per = run_timed(torch, rbs, steps, warmup)
-    # verify + rollback as one serving step
-    both = [lambda f=f, r=r: (f(), r()) for f, r in zip(fwd, rbs)]
-    b_ms, _ = run_timed(torch, both, steps, warmup)
+    vt = _timing(*run_timed(torch, fwd, steps, warmup), steps)
+    rt = _timing(*run_timed(torch, rbs, steps, warmup), steps)
+    bt = _timing(*run_timed(torch, pair, steps, warmup), steps)
     vbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, case.K, kda, True)
     moved = int(np.count_nonzero(case.accepted > 0))
     rbytes = 2 * moved * case.H * 4 * case.d_k * case.d_v
-    vs, rs = stats(v_per), stats(r_per)
     tokens = case.B * case.T
+    vg = vbytes / (vt["us_per_launch"] * 1e-6) / 1e9
+    rg = rbytes / (rt["us_per_launch"] * 1e-6) / 1e9
     out = dict(
         workload=gi.CONFIGS[cfg]["name"],
-        verify=dict(bytes=vbytes, launch=vs, achieved_gbs=vbytes / (vs["mean_us"] * 1e-6) / 1e9,
-                    tokens_per_s=tokens * steps / (v_ms * 1e-3)),
-        rollback=dict(bytes=rbytes, sequences_rolled=moved, launch=rs,
-                      achieved_gbs=rbytes / (rs["mean_us"] * 1e-6) / 1e9),
-        verify_plus_rollback=dict(ms_per_step=b_ms / steps,
-                                  tokens_per_s=tokens * steps / (b_ms * 1e-3)),
-        n_sets=n_sets,
+        verify=dict(bytes=vbytes, achieved_gbs=vg, frac_of_hbm_peak=vg / HBM_PEAK_GBS,
+                    tokens_per_s=tokens / (vt["us_per_launch"] * 1e-6), **vt),
+        rollback=dict(bytes=rbytes, sequences_rolled=moved, achieved_gbs=rg,
+                      frac_of_hbm_peak=rg / HBM_PEAK_GBS, **rt),
+        verify_plus_rollback=dict(tokens_per_s=tokens / (bt["us_per_launch"] * 1e-6), **bt),
+        rotating_sets=len(sets),
     )
-    for key in ("verify", "rollback"):
-        out[key]["frac_of_hbm_peak"] = out[key]["achieved_gbs"] / HBM_PEAK_GBS
-    del sets
+    del sets, fwd, rbs, pair
+    torch.cuda.empty_cache()
     return out
 
 
-def bench_prefill(torch, lib, stream, steps, warmup):
+def bench_prefill(torch, lib, steps, warmup):
     import gdn_inputs as gi
     case = gi.config_case(4)
     d = upload_case(torch, case)
     st0 = d["state"][:, :, 0].contiguous()
     ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
     args = (case.B, case.T, case.H, case.d_k, case.d_v, 64, vp(d["q"]), vp(d["k"]), vp(d["v"]),
-            vp(d["g"]), vp(d["beta"]), vp(st0), vp(o), vp(ws), ws_bytes, stream)
+            vp(d["g"]), vp(d["beta"]), vp(st0), vp(o), vp(ws), ws_bytes)
 
-    def call():
-        s = lib.gdn_prefill_chunked(*args)
+    def call(stream):
+        s = lib.gdn_prefill_chunked(*args, stream)
         if s != 0:
             raise RuntimeError(f"libgdn status {s}")
-    region_ms, per = run_timed(torch, [call], steps, warmup)
-    s = stats(per)
-    t = s["mean_us"] * 1e-6
+    t = _timing(*run_timed(torch, [call], steps, warmup), steps)
+    sec = t["us_per_launch"] * 1e-6
     nb = prefill_bytes(case.B, case.T, case.H, case.d_k)
     fl = prefill_flops(case.B, case.T, case.H, case.d_k)
     return dict(
-        workload=gi.CONFIGS[4]["name"], launch=s, bytes=nb, flops=fl,
-        tokens_per_s=case.B * case.T / t,
-        achieved_gbs=nb / t / 1e9, frac_of_hbm_peak=nb / t / 1e9 / HBM_PEAK_GBS,
-        achieved_tflops=fl / t / 1e12, frac_of_bf16_peak=fl / t / 1e12 / BF16_PEAK_TFLOPS,
-        workspace_bytes=int(ws_bytes),
+        workload=gi.CONFIGS[4]["name"], bytes=nb, flops=fl,
+        tokens_per_s=case.B * case.T / sec,
+        achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
+        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
+        workspace_bytes=int(ws_bytes), **t,
     )
 
 
@@ -312,22 +316,23 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     log("device:", torch.cuda.get_device_name(0))
 
     log("decode ...")
-    dec = bench_decode(torch, lib, stream, args.steps, args.warmup)
-    log(f"decode: {dec['launch']['mean_us']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s")
+    dec = bench_decode(torch, lib, args.steps, args.warmup)
+    log(f"decode: {dec['us_per_launch']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s "
+        f"(eager {dec['eager_us_per_launch']:.2f} us)")
     paths = {}
     if args.only == "all":
         for cfg in (2, 3):
             log(f"verify config {cfg} ...")
-            paths[f"verify_rollback_{'gda' if cfg == 2 else 'kda'}"] = bench_verify(
-                torch, lib, stream, cfg, args.steps, args.warmup)
+            r = bench_verify(torch, lib, cfg, args.steps, args.warmup)
+            paths[f"verify_rollback_{'gda' if cfg == 2 else 'kda'}"] = r
+            log(f"  verify {r['verify']['us_per_launch']:.2f} us {r['verify']['achieved_gbs']:.0f} GB/s; "
+                f"rollback {r['rollback']['us_per_launch']:.2f} us {r['rollback']['achieved_gbs']:.0f} GB/s")
         log("prefill ...")
         try:
-            paths["prefill_chunked_gda"] = bench_prefill(torch, lib, stream,
-                                                         max(5, args.steps // 10),
+            paths["prefill_chunked_gda"] = bench_prefill(torch, lib, max(5, args.steps // 10),
                                                          max(2, args.warmup // 10))
         except RuntimeError as e:
             paths["prefill_chunked_gda"] = {"error": str(e)}
@@ -363,9 +368,10 @@ def main():
             "unit": "GB/s",
             "frac": dec["achieved_gbs"] / HBM_PEAK_GBS,
             "traffic": None,
-            "kernel": "gdn::recurrent_kernel<128, GDA, bf16>",
+            "kernel": "gdn::recurrent_kernel<128, GDA, bf16, single token>",
             "bytes_per_launch": dec["bytes"],
-            "launch_us": dec["launch"],
+            "us_per_launch": dec["us_per_launch"],
+            "eager_us_per_launch": dec["eager_us_per_launch"],
         },
         "cpu_baseline": cpu,
         "paths": paths,

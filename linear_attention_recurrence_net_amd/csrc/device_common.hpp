@@ -31,13 +31,12 @@ __device__ __forceinline__ void unpack_bf16x2(uint32_t w, float& lo, float& hi) 
     hi = __uint_as_float(w & 0xffff0000u);
 }
 
-// Load N consecutive elements (float32 or bf16) as float32.  The address of
-// the first element must be aligned to 16 bytes and N * sizeof(elem) a
-// multiple of 16.
+// Load N consecutive elements (float32 or bf16) as float32.  The first
+// element must be aligned to the vector width used (16 bytes for float32 and
+// for 8 bf16 values, 8 bytes for 4 bf16 values).
 template <int N, bool BF16>
 __device__ __forceinline__ void load_vec(const void* base, size_t offset, float (&out)[N]) {
-    if constexpr (BF16) {
-        static_assert(N % 8 == 0, "bf16 vector loads move 8 values at a time");
+    if constexpr (BF16 && N % 8 == 0) {
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + offset);
 #pragma unroll
         for (int i = 0; i < N / 8; ++i) {
@@ -46,6 +45,15 @@ __device__ __forceinline__ void load_vec(const void* base, size_t offset, float 
             unpack_bf16x2(w.y, out[8 * i + 2], out[8 * i + 3]);
             unpack_bf16x2(w.z, out[8 * i + 4], out[8 * i + 5]);
             unpack_bf16x2(w.w, out[8 * i + 6], out[8 * i + 7]);
+        }
+    } else if constexpr (BF16) {
+        static_assert(N % 4 == 0, "bf16 vector loads move 4 or 8 values at a time");
+        const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + offset);
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            uint2 w = p[i];
+            unpack_bf16x2(w.x, out[4 * i + 0], out[4 * i + 1]);
+            unpack_bf16x2(w.y, out[4 * i + 2], out[4 * i + 3]);
         }
     } else {
         static_assert(N % 4 == 0, "float32 vector loads move 4 values at a time");
@@ -98,8 +106,18 @@ __device__ __forceinline__ float add_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 8 lanes that differ in lane bits 3..5 (lane ^ 8, ^16, ^32).
-__device__ __forceinline__ float sum_over_rowgroups(float x) {
+//   xor 4  : ds_swizzle in bitmask mode (and 0x1f, xor 4) inside 32 lanes
+__device__ __forceinline__ float add_xor4(float x) {
+    int y = __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1f | (4 << 10));
+    return x + __int_as_float(y);
+}
+
+// Sum over the lanes that share lane % FROM, i.e. the butterfly over lane
+// bits log2(FROM)..5.  FROM is 4 or 8.
+template <int FROM>
+__device__ __forceinline__ float sum_lanes_from(float x) {
+    static_assert(FROM == 4 || FROM == 8, "row-group stride");
+    if constexpr (FROM == 4) x = add_xor4(x);
     return add_xor32(add_xor16(add_xor8(x)));
 }
 

@@ -204,3 +204,36 @@ def test_rollback_any_tile(d_k, d_v):
     torch.cuda.synchronize()
     ref, _ = oracle.rollback(acc_np, st_np.astype(np.float64))
     assert np.array_equal(st.cpu().numpy().view(np.int32), ref.astype(np.float32).view(np.int32))
+
+
+def test_graph_replay_matches_eager():
+    """The bench times HIP-graph replays of these launches: every replay must
+    equal the eager result bit for bit, with eager work between replays."""
+    c = gi.make_case(8, 4, 4, 128, K=4, gate="gda", seed=77, with_accepted=True)
+    d = upload(c)
+    acc = torch.from_numpy(c.accepted).to("cuda")
+    base = d["state"].clone()
+    gdn = _gdn()
+
+    work = base.clone()
+    o = torch.empty((c.B, c.T, c.H, c.d_v), device="cuda")
+    gdn.gdn_forward_snapshots(d["q"], d["k"], d["v"], d["g"], d["beta"], work, None, o)
+    gdn.gdn_rollback_select(acc, work)
+    torch.cuda.synchronize()
+    ref_o, ref_s = bits(o), bits(work)
+
+    work2 = torch.empty_like(base)
+    o2 = torch.empty_like(o)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        torch.mul(base, 1.0, out=work2)  # reset the state with a kernel (x * 1 is exact)
+        gdn.gdn_forward_snapshots(d["q"], d["k"], d["v"], d["g"], d["beta"], work2, None, o2)
+        gdn.gdn_rollback_select(acc, work2)
+    for _ in range(3):
+        work2.fill_(float("nan"))
+        o2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o2), ref_o)
+        assert np.array_equal(bits(work2), ref_s)
