@@ -199,8 +199,9 @@ def gdn_prefill_chunked(q, k, v, g, beta, state, o=None, workspace=None, chunk: 
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     _dev_tensor("o", o, (torch.float32,), dev)
     _shape("o", o, (B, T, H, dv))
-    if gate != GDN_GATE_HEAD:
-        raise GdnError("gdn_prefill_chunked", 3, "chunked prefill supports GDA gates only")
+    if gate != GDN_GATE_HEAD or dt != GDN_BF16:
+        raise GdnError("gdn_prefill_chunked", 3,
+                       "chunked prefill supports GDA gates with bfloat16 q/k/v only")
     need = gdn_prefill_workspace_size(B, T, H, dk, dv, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
