@@ -300,7 +300,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "all"], default="all")
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "all"], default="all",
+                    help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the GDN path is "
@@ -318,24 +319,30 @@ def main():
         sys.exit(1)
     log("device:", torch.cuda.get_device_name(0))
 
-    log("decode ...")
-    dec = bench_decode(torch, lib, args.steps, args.warmup)
-    log(f"decode: {dec['us_per_launch']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s "
-        f"(eager {dec['eager_us_per_launch']:.2f} us)")
+    dec = None
+    if args.only in ("decode", "all"):
+        log("decode ...")
+        dec = bench_decode(torch, lib, args.steps, args.warmup)
+        log(f"decode: {dec['us_per_launch']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s "
+            f"(eager {dec['eager_us_per_launch']:.2f} us)")
     paths = {}
-    if args.only == "all":
+    if args.only in ("verify", "all"):
         for cfg in (2, 3):
             log(f"verify config {cfg} ...")
             r = bench_verify(torch, lib, cfg, args.steps, args.warmup)
             paths[f"verify_rollback_{'gda' if cfg == 2 else 'kda'}"] = r
             log(f"  verify {r['verify']['us_per_launch']:.2f} us {r['verify']['achieved_gbs']:.0f} GB/s; "
                 f"rollback {r['rollback']['us_per_launch']:.2f} us {r['rollback']['achieved_gbs']:.0f} GB/s")
+    if args.only in ("prefill", "all"):
         log("prefill ...")
-        try:
-            paths["prefill_chunked_gda"] = bench_prefill(torch, lib, max(5, args.steps // 10),
-                                                         max(2, args.warmup // 10))
-        except RuntimeError as e:
-            paths["prefill_chunked_gda"] = {"error": str(e)}
+        steps = args.steps if args.only == "prefill" else max(5, args.steps // 10)
+        warm = args.warmup if args.only == "prefill" else max(2, args.warmup // 10)
+        paths["prefill_chunked_gda"] = r = bench_prefill(torch, lib, steps, warm)
+        log(f"  prefill {r['us_per_launch']:.1f} us, {r['achieved_tflops']:.1f} TFLOP/s, "
+            f"{r['achieved_gbs']:.0f} GB/s")
+    if dec is None:
+        print(json.dumps({"partial_run": args.only, "paths": paths}), flush=True)
+        return
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -105,7 +105,8 @@ int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_
  * chunked fused GDN path"; the chunk algebra is the WY/UT form of the same
  * recurrence and gives the same result up to rounding).
  * GDA only, q/k/v bfloat16, d_k = d_v in {64,128}, chunk = 64, any T >= 0
- * (a short final chunk behaves as if padded with beta = 0, g = 0, k = q = v = 0).
+ * with T*H*d_k*4 < 2^31 bytes per sequence (a short final chunk behaves as if
+ * padded with beta = 0, g = 0, k = q = v = 0).
  * state [B,H,d_k,d_v] float32 holds S_0 on entry and S_T on return;
  * o [B,T,H,d_v] float32.  Contractions run on bf16 MFMA with float32
  * accumulation; the carried state stays float32.

@@ -101,6 +101,8 @@ int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
         return GDN_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || T == 0) return GDN_OK;
+    // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
+    if (static_cast<int64_t>(T) * H * d_k * 4 >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
     const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)

@@ -43,13 +43,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Workspace block of one (sequence, head, chunk).
-constexpr size_t kWsT1Hi = 0;
-constexpr size_t kWsT1Lo = kC * kC * 2;
-constexpr size_t kWsQkHi = 2 * kC * kC * 2;
-constexpr size_t kWsQkLo = 3 * kC * kC * 2;
-constexpr size_t kWsG = 4 * kC * kC * 2;
-constexpr size_t kWsBlock = kWsG + kC * 4;  // 33024 bytes, a multiple of 256
+// Workspace: one block per (sequence, head, chunk): T1 and QKm as bf16 hi/lo
+// (row-major 64 x 64) and the gate factors exp(G_r), exp(G_last - G_r) and
+// exp(G_last) in fp32.
+constexpr int kWsT1Hi = 0;
+constexpr int kWsT1Lo = kC * kC * 2;
+constexpr int kWsQkHi = 2 * kC * kC * 2;
+constexpr int kWsQkLo = 3 * kC * kC * 2;
+constexpr int kWsEG = 4 * kC * kC * 2;     // exp(G_r)
+constexpr int kWsER = kWsEG + kC * 4;      // exp(G_last - G_r)
+constexpr int kWsEL = kWsER + kC * 4;      // exp(G_last)
+constexpr int kWsBlock = kWsEL + 256;      // 33536 bytes, a multiple of 256
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -80,11 +84,32 @@ __device__ __forceinline__ u32x2 pack4(const uint32_t (&h)[4]) {
     return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Four floats -> packed bf16 (4 values in 2 words).
+__device__ __forceinline__ u32x2 to_bf16x4(float a, float b, float c, float d) {
+    return u32x2{cvt2(a, b), cvt2(c, d)};
+}
+
+// Four floats x = hi + lo, hi and lo packed bf16 (both round to nearest).
+__device__ __forceinline__ void split4(float a, float b, float c, float d, u32x2& hi, u32x2& lo) {
+    hi = to_bf16x4(a, b, c, d);
+    lo = to_bf16x4(a - __uint_as_float(hi[0] << 16), b - __uint_as_float(hi[0] & 0xffff0000u),
+                    c - __uint_as_float(hi[1] << 16), d - __uint_as_float(hi[1] & 0xffff0000u));
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int B, int T, int H, int d) {
     (void)d;
-    const size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
+    size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
+    nc += nc & 1;  // an even chunk count (see launch_prefill_t)
     return static_cast<size_t>(B) * H * nc * kWsBlock;
 }
 
@@ -128,7 +153,12 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     sG[lane] = G;
     sBeta[lane] = bv;
     char* wsb = ws + static_cast<size_t>(blk) * kWsBlock;
-    reinterpret_cast<float*>(wsb + kWsG)[lane] = G;
+    {
+        const float Glast = __shfl(G, 63, 64);
+        reinterpret_cast<float*>(wsb + kWsEG)[lane] = expf(G);
+        reinterpret_cast<float*>(wsb + kWsER)[lane] = expf(Glast - G);
+        if (lane == 0) reinterpret_cast<float*>(wsb + kWsEL)[0] = expf(Glast);
+    }
 
     // fragments of the chunk's k rows (zero beyond the sequence end)
     auto row_ptr = [&](const uint16_t* base, int r) {
@@ -207,14 +237,33 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution, one column per lane, in fp32
+    // T = (I + A)^-1 by forward substitution, one column per lane, in fp32,
+    // in blocks of 16 rows: first the contributions of all earlier blocks
+    // (16 independent sums), then the sequential triangle of the block.
     float x[kC];
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-        float acc = (r == lane) ? 1.f : 0.f;
+    for (int I = 0; I < kC / 16; ++I) {
+        float y[16];
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc = fmaf(-sA[r][s], x[s], acc);
-        x[r] = acc;
+        for (int i = 0; i < 16; ++i) y[i] = (16 * I + i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int s4 = 0; s4 < 16 * I; s4 += 4) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[16 * I + i][s4]);
+                y[i] = fmaf(-a.x, x[s4], y[i]);
+                y[i] = fmaf(-a.y, x[s4 + 1], y[i]);
+                y[i] = fmaf(-a.z, x[s4 + 2], y[i]);
+                y[i] = fmaf(-a.w, x[s4 + 3], y[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = y[i];
+#pragma unroll
+            for (int s = 16 * I; s < 16 * I + i; ++s) acc = fmaf(-sA[16 * I + i][s], x[s], acc);
+            x[16 * I + i] = acc;
+        }
     }
     // T1 = T diag(beta): scale this lane's column, store as hi/lo bf16
     uint16_t* t1h = reinterpret_cast<uint16_t*>(wsb + kWsT1Hi);
@@ -232,6 +281,19 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 // chain: one workgroup (4 wavefronts) per (sequence, head, 16-column block)
 // ---------------------------------------------------------------------------
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zeros and stores past the end are dropped (the hardware range check), which
+// handles the rows after the end of a sequence without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes > 0 ? bytes : 0,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)));
+}
+
 template <int D>
 __global__ void __launch_bounds__(256)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -251,6 +313,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __shared__ __attribute__((aligned(16))) uint16_t sR[2][16][CLD];
     __shared__ __attribute__((aligned(16))) uint16_t sW[2][16][CLD];
     __shared__ __attribute__((aligned(16))) uint16_t sWp[2][16][CLD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][16][CLD];  // V block, [col][row]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -263,7 +326,26 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int h = bh - b * H;
     const int col = cb * 16 + lr;
 
-    auto tok = [&](int t) { return (static_cast<size_t>(b) * T + t) * H + h; };
+    // per (sequence, head) views; a token row is H*D elements apart
+    const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;  // element of (b, t=0, h, 0)
+    const int row_b16 = H * D * 2;                                  // bytes per token, bf16
+    const int seq_b16 = (T - 1) * row_b16 + D * 2;  // bytes of the last valid row's end
+
+    // per-lane byte offsets inside a chunk (constant over the chunks)
+    int koff[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int piece = tid + 256 * i;
+        koff[i] = (piece / (D / 8)) * row_b16 + (piece % (D / 8)) * 16;
+    }
+    const int ra = 16 * wave + lr;  // A-operand row of this lane
+    const int qoff = ra * row_b16 + 16 * grp;
+    const int woff = (ra * kC + 8 * grp) * 2;
+    // V block of the chunk (64 rows x 16 columns): one 8-byte piece per thread
+    const int vrow = tid >> 2, vq = tid & 3;
+    const int voff = vrow * row_b16 + (cb * 16 + 4 * vq) * 2;
+    const int goff = (16 * wave + 4 * grp) * 4;  // this lane's rows in the gate-factor arrays
+    float* const obase = o + head0 + static_cast<size_t>(16 * wave + 4 * grp) * H * D + col;
 
     // ---- initial state block (fp32, accumulator layout) --------------------
     float* st = state + static_cast<size_t>(bh) * D * D;
@@ -276,12 +358,9 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     auto write_state_lds = [&]() {
 #pragma unroll
-        for (int mt = 0; mt < SMT; ++mt) {
-            uint32_t hb[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) hb[rr] = bf16_rne(S[mt][rr]);
-            *reinterpret_cast<u32x2*>(&sS[lr][wave * SROWS + 16 * mt + 4 * grp]) = pack4(hb);
-        }
+        for (int mt = 0; mt < SMT; ++mt)
+            *reinterpret_cast<u32x2*>(&sS[lr][wave * SROWS + 16 * mt + 4 * grp]) =
+                to_bf16x4(S[mt][0], S[mt][1], S[mt][2], S[mt][3]);
     };
 
     // ---- per-chunk operands held in registers ------------------------------
@@ -290,43 +369,42 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         bf16x8 qf[KS];         // Q rows 16*wave.. (A operand)
         bf16x8 t1h[2], t1l[2]; // T1 rows 16*wave.. hi/lo
         bf16x8 qkh[2], qkl[2]; // QKm rows 16*wave.. hi/lo
-        float vv[4];           // V at rows 16*wave + 4*grp + rr, column col
-        float G[4];            // G at the same rows
-        float Glast;
+        u32x2 vpiece;          // 4 bf16 of V, staged to LDS
+        f32x4 eg;              // exp(G) at rows 16*wave + 4*grp + 0..3
+        f32x4 er;              // exp(G_last - G) at the same rows
+        float el;              // exp(G_last)
     };
 
+    // Loads of chunk n's operands: buffer loads with constant per-lane
+    // offsets from per-chunk (scalar) resources; rows past the sequence end
+    // come back as zeros.
     auto load_ops = [&](int n, Ops& p) {
-        const int t0 = n * kC;
-        const int nvalid = min(kC, T - t0);
+        const int cbyte = n * kC;  // first token of the chunk
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head0 + static_cast<size_t>(cbyte) * H * D,
+                                                     seq_b16 - cbyte * row_b16);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head0 + static_cast<size_t>(cbyte) * H * D,
+                                                     seq_b16 - cbyte * row_b16);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head0 + static_cast<size_t>(cbyte) * H * D,
+                                                     seq_b16 - cbyte * row_b16);
+        const __amdgpu_buffer_rsrc_t rw =
+            make_rsrc(ws + (static_cast<size_t>(bh) * NC + n) * kWsBlock, kWsBlock);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int piece = tid + 256 * i;
-            const int r = piece / (D / 8);
-            const int c8 = piece % (D / 8);
-            p.kpiece[i] = r < nvalid ? *reinterpret_cast<const u32x4*>(k + tok(t0 + r) * D + 8 * c8)
-                                     : u32x4{0u, 0u, 0u, 0u};
-        }
-        const int ra = 16 * wave + lr;  // A-operand row of this lane
+        for (int i = 0; i < KPT; ++i)
+            p.kpiece[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0));
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            p.qf[ks] = ra < nvalid ? ld16_bf16(q + tok(t0 + ra) * D + 32 * ks + 8 * grp) : zero_bf16x8();
-        const char* wsb = ws + (static_cast<size_t>(bh) * NC + n) * kWsBlock;
+        for (int ks = 0; ks < KS; ++ks) p.qf[ks] = buf_ld16(rq, qoff + 64 * ks);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const size_t off = (static_cast<size_t>(ra) * kC + 32 * ks + 8 * grp) * 2;
-            p.t1h[ks] = ld16_bf16(wsb + kWsT1Hi + off);
-            p.t1l[ks] = ld16_bf16(wsb + kWsT1Lo + off);
-            p.qkh[ks] = ld16_bf16(wsb + kWsQkHi + off);
-            p.qkl[ks] = ld16_bf16(wsb + kWsQkLo + off);
+            p.t1h[ks] = buf_ld16(rw, kWsT1Hi + woff + 64 * ks);
+            p.t1l[ks] = buf_ld16(rw, kWsT1Lo + woff + 64 * ks);
+            p.qkh[ks] = buf_ld16(rw, kWsQkHi + woff + 64 * ks);
+            p.qkl[ks] = buf_ld16(rw, kWsQkLo + woff + 64 * ks);
         }
-        const float* Gp = reinterpret_cast<const float*>(wsb + kWsG);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = 16 * wave + 4 * grp + rr;
-            p.vv[rr] = r < nvalid ? bf16_to_f32(v[tok(t0 + r) * D + col]) : 0.f;
-            p.G[rr] = Gp[r];
-        }
-        p.Glast = Gp[kC - 1];
+        p.vpiece = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0));
+        p.eg = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kWsEG + goff, 0, 0));
+        p.er = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kWsER + goff, 0, 0));
+        // uniform address: a scalar load
+        p.el = *reinterpret_cast<const float*>(ws + (static_cast<size_t>(bh) * NC + n) * kWsBlock + kWsEL);
     };
 
     auto stage_k = [&](const Ops& p, int buf) {
@@ -337,19 +415,34 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const int c8 = piece % (D / 8);
             *reinterpret_cast<u32x4*>(&sK[buf][r][8 * c8]) = p.kpiece[i];
         }
+        sV[buf][4 * vq + 0][vrow] = static_cast<uint16_t>(p.vpiece[0]);
+        sV[buf][4 * vq + 1][vrow] = static_cast<uint16_t>(p.vpiece[0] >> 16);
+        sV[buf][4 * vq + 2][vrow] = static_cast<uint16_t>(p.vpiece[1]);
+        sV[buf][4 * vq + 3][vrow] = static_cast<uint16_t>(p.vpiece[1] >> 16);
     };
 
-    Ops cur, nxt;
-    load_ops(0, cur);
-    stage_k(cur, 0);
-    write_state_lds();
+    // K^T fragment (rows dk0..dk0+15 of d_k, chunk rows 32*ks + 8*grp + 0..7)
+    // from the row-major K chunk with two transposing LDS reads: source lane
+    // s of each 16-lane group points at K[r0 + s/4][dk0 + 4*(s%4)], and lane
+    // i receives K[r0 + j][dk0 + i] for j = 0..3.
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    auto kt_frag = [&](int buf, int dk0, int ks) {
+        const int r0 = 32 * ks + 8 * grp + (lr >> 2);
+        const int c0 = dk0 + 4 * (lr & 3);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(&sK[buf][r0][c0]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(&sK[buf][r0 + 4][c0]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+    };
 
-    for (int n = 0; n < NC; ++n) {
+    // One chunk: the state chain (X, R, W, S) first, then the outputs.
+    auto step = [&](int n, const Ops& cur, Ops& nxt) {
         const int buf = n & 1;
-        const int t0 = n * kC;
-        const int nvalid = min(kC, T - t0);
         __syncthreads();  // sK[buf] and sS hold chunk n's K and the chunk start state
-        if (n + 1 < NC) load_ops(n + 1, nxt);
+        load_ops(min(n + 1, NC - 1), nxt);  // prefetch (the last chunk reloads itself)
 
         // X = K S and P = Q S for rows 16*wave.. of the chunk
         f32x4 X = {0.f, 0.f, 0.f, 0.f};
@@ -363,16 +456,15 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         }
 
         // R = V - exp(G) X  ->  LDS as hi/lo, transposed [col][row]
-        float eg[4];
         {
-            uint32_t rh[4], rl[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                eg[rr] = expf(cur.G[rr]);
-                split_bf16(cur.vv[rr] - eg[rr] * X[rr], rh[rr], rl[rr]);
-            }
-            *reinterpret_cast<u32x2*>(&sR[0][lr][16 * wave + 4 * grp]) = pack4(rh);
-            *reinterpret_cast<u32x2*>(&sR[1][lr][16 * wave + 4 * grp]) = pack4(rl);
+            const u32x2 vv = *reinterpret_cast<const u32x2*>(&sV[buf][lr][16 * wave + 4 * grp]);
+            u32x2 rh, rl;
+            split4(__uint_as_float(vv[0] << 16) - cur.eg[0] * X[0],
+                   __uint_as_float(vv[0] & 0xffff0000u) - cur.eg[1] * X[1],
+                   __uint_as_float(vv[1] << 16) - cur.eg[2] * X[2],
+                   __uint_as_float(vv[1] & 0xffff0000u) - cur.eg[3] * X[3], rh, rl);
+            *reinterpret_cast<u32x2*>(&sR[0][lr][16 * wave + 4 * grp]) = rh;
+            *reinterpret_cast<u32x2*>(&sR[1][lr][16 * wave + 4 * grp]) = rl;
         }
         __syncthreads();
 
@@ -387,24 +479,38 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             W = mfma(cur.t1l[ks], bh_, W);
         }
         {
-            uint32_t wh[4], wl[4], ph[4], pl[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                split_bf16(W[rr], wh[rr], wl[rr]);
-                split_bf16(expf(cur.Glast - cur.G[rr]) * W[rr], ph[rr], pl[rr]);
-            }
-            *reinterpret_cast<u32x2*>(&sW[0][lr][16 * wave + 4 * grp]) = pack4(wh);
-            *reinterpret_cast<u32x2*>(&sW[1][lr][16 * wave + 4 * grp]) = pack4(wl);
-            *reinterpret_cast<u32x2*>(&sWp[0][lr][16 * wave + 4 * grp]) = pack4(ph);
-            *reinterpret_cast<u32x2*>(&sWp[1][lr][16 * wave + 4 * grp]) = pack4(pl);
+            u32x2 wh, wl, ph, pl;
+            split4(W[0], W[1], W[2], W[3], wh, wl);
+            split4(cur.er[0] * W[0], cur.er[1] * W[1], cur.er[2] * W[2], cur.er[3] * W[3], ph, pl);
+            *reinterpret_cast<u32x2*>(&sW[0][lr][16 * wave + 4 * grp]) = wh;
+            *reinterpret_cast<u32x2*>(&sW[1][lr][16 * wave + 4 * grp]) = wl;
+            *reinterpret_cast<u32x2*>(&sWp[0][lr][16 * wave + 4 * grp]) = ph;
+            *reinterpret_cast<u32x2*>(&sWp[1][lr][16 * wave + 4 * grp]) = pl;
         }
         __syncthreads();
+
+        // S <- exp(G_last) S + K^T W'
+#pragma unroll
+        for (int mt = 0; mt < SMT; ++mt) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= cur.el;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 aKt = kt_frag(buf, wave * SROWS + 16 * mt, ks);
+                const bf16x8 bh_ = ld16_bf16(&sWp[0][lr][32 * ks + 8 * grp]);
+                const bf16x8 bl_ = ld16_bf16(&sWp[1][lr][32 * ks + 8 * grp]);
+                S[mt] = mfma(aKt, bh_, S[mt]);
+                S[mt] = mfma(aKt, bl_, S[mt]);
+            }
+        }
+        // no wavefront reads sS past the barriers above
+        write_state_lds();
 
         // O = exp(G) P + QKm W
         {
             f32x4 O;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) O[rr] = eg[rr] * P[rr];
+            for (int rr = 0; rr < 4; ++rr) O[rr] = cur.eg[rr] * P[rr];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x8 bh_ = ld16_bf16(&sW[0][lr][32 * ks + 8 * grp]);
@@ -413,43 +519,25 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 O = mfma(cur.qkh[ks], bl_, O);
                 O = mfma(cur.qkl[ks], bh_, O);
             }
+            // plain global stores (the raw buffer store builtin miscompiles
+            // element extraction from accumulator registers here)
+            const int t0 = n * kC;
+            float* orow = obase + static_cast<size_t>(t0) * H * D;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = 16 * wave + 4 * grp + rr;
-                if (r < nvalid) o[tok(t0 + r) * D + col] = O[rr];
-            }
+            for (int rr = 0; rr < 4; ++rr)
+                if (t0 + 16 * wave + 4 * grp + rr < T) orow[rr * static_cast<size_t>(H) * D] = O[rr];
         }
+        stage_k(nxt, buf ^ 1);  // sK[buf ^ 1] was last read in the previous chunk
+    };
 
-        // S <- exp(G_last) S + K^T W'   (K^T gathered from the staged chunk)
-        {
-            const float el = expf(cur.Glast);
-#pragma unroll
-            for (int mt = 0; mt < SMT; ++mt) {
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= el;
-                const int dk_row = wave * SROWS + 16 * mt + lr;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    uint32_t e[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) e[j] = sK[buf][32 * ks + 8 * grp + j][dk_row];
-                    const bf16x8 aKt = as_bf16x8(u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16),
-                                                       e[4] | (e[5] << 16), e[6] | (e[7] << 16)});
-                    const bf16x8 bh_ = ld16_bf16(&sWp[0][lr][32 * ks + 8 * grp]);
-                    const bf16x8 bl_ = ld16_bf16(&sWp[1][lr][32 * ks + 8 * grp]);
-                    S[mt] = mfma(aKt, bh_, S[mt]);
-                    S[mt] = mfma(aKt, bl_, S[mt]);
-                }
-            }
-        }
-
-        // chunk n + 1: state and K into LDS (no wavefront reads sS or
-        // sK[buf ^ 1] past the barriers above)
-        write_state_lds();
-        if (n + 1 < NC) {
-            stage_k(nxt, buf ^ 1);
-            cur = nxt;
-        }
+    // Two operand buffers used in turn (no register copies between chunks).
+    Ops opa, opb;
+    load_ops(0, opa);
+    stage_k(opa, 0);
+    write_state_lds();
+    for (int n = 0; n < NC; n += 2) {  // NC is even
+        step(n, opa, opb);
+        step(n + 1, opb, opa);
     }
 
 #pragma unroll
@@ -461,7 +549,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 template <int D>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    const int NC = (a.T + kC - 1) / kC;
+    // An odd chunk count gets one more chunk past the sequence end: all its
+    // rows read zeros and beta = g = 0 there, so it leaves the state exactly
+    // unchanged (exp(0) S + K^T 0) and writes no output.  The chain then
+    // walks chunks in pairs with two operand buffers.
+    int NC = (a.T + kC - 1) / kC;
+    NC += NC & 1;
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     char* ws = static_cast<char*>(a.workspace);
     hipLaunchKernelGGL(prefill_prep_kernel<D>, dim3(bh * NC), dim3(64), 0, stream,
