@@ -40,6 +40,41 @@ ROTATE_BYTES = 1 << 30  # >= 1 GiB of rotating buffers defeats the 256 MB MALL
 
 METRIC = "GDN tokens/s and achieved HBM GB/s (% peak), decode B=64 H=16 d=128"
 
+# HBM traffic of one decode launch, from two rocprofv3 --pmc runs of
+# `bench.py --only decode --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch; summary in profiles/recurrent_decode_B64_H16_d128_traffic.md).
+# Each counter is scaled by what it reads for a 64 MiB device-to-device copy
+# (64 MiB read + 64 MiB written).  The figures describe the kernel built from
+# the sources hashed below and are reported only while those are unchanged.
+DECODE_TRAFFIC = {
+    "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
+                "linear_attention_recurrence_net_amd/csrc/device_common.hpp"],
+    "sha256": "102cfd493ae620c62c5cd28287bb3bb3b1030e5e2b7c8d9c60628a511604cd7f",
+    "fetch_kib": 33506.0,       # median over 62 decode dispatches
+    "write_kib": 66079.0625,
+    "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
+    "copy_write_kib": 65536.0,
+}
+
+
+def decode_traffic_bytes():
+    """Calibrated HBM bytes per decode launch, or None if not measured for
+    the current kernel sources."""
+    import hashlib
+    t = DECODE_TRAFFIC
+    if t["sha256"] is None:
+        return None
+    h = hashlib.sha256()
+    for rel in t["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != t["sha256"]:
+        return None
+    copy_bytes = 64 * 1024 * 1024
+    fetch = t["fetch_kib"] * 1024 * copy_bytes / (t["copy_fetch_kib"] * 1024)
+    write = t["write_kib"] * 1024 * copy_bytes / (t["copy_write_kib"] * 1024)
+    return fetch + write
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -177,7 +212,7 @@ def _timing(region_ms, eager_ms, steps):
 
 def bench_decode(torch, lib, steps, warmup):
     import gdn_inputs as gi
-    case = gi.config_case(1)
+    case = gi.workload_case(1)
     d = upload_case(torch, case)
     sets = _rotating_sets(torch, d, case, with_state_slot0=True)
     calls = [raw_forward_call(lib, case, s, s["state"], s["o"]) for s in sets]
@@ -195,7 +230,7 @@ def bench_decode(torch, lib, steps, warmup):
 def bench_verify(torch, lib, cfg, steps, warmup):
     """Speculative verify (K=4 snapshots, no final state), then rollback."""
     import gdn_inputs as gi
-    case = gi.config_case(cfg)
+    case = gi.workload_case(cfg)
     d = upload_case(torch, case)
     sets = _rotating_sets(torch, d, case)
     acc = torch.from_numpy(case.accepted).to("cuda")
@@ -229,7 +264,7 @@ def bench_verify(torch, lib, cfg, steps, warmup):
     vg = vbytes / (vt["us_per_launch"] * 1e-6) / 1e9
     rg = rbytes / (rt["us_per_launch"] * 1e-6) / 1e9
     out = dict(
-        workload=gi.CONFIGS[cfg]["name"],
+        workload=gi.WORKLOADS[cfg]["name"],
         verify=dict(bytes=vbytes, achieved_gbs=vg, frac_of_hbm_peak=vg / HBM_PEAK_GBS,
                     tokens_per_s=tokens / (vt["us_per_launch"] * 1e-6), **vt),
         rollback=dict(bytes=rbytes, sequences_rolled=moved, achieved_gbs=rg,
@@ -244,7 +279,7 @@ def bench_verify(torch, lib, cfg, steps, warmup):
 
 def bench_prefill(torch, lib, steps, warmup):
     import gdn_inputs as gi
-    case = gi.config_case(4)
+    case = gi.workload_case(4)
     d = upload_case(torch, case)
     st0 = d["state"][:, :, 0].contiguous()
     ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
@@ -263,7 +298,7 @@ def bench_prefill(torch, lib, steps, warmup):
     nb = prefill_bytes(case.B, case.T, case.H, case.d_k)
     fl = prefill_flops(case.B, case.T, case.H, case.d_k)
     return dict(
-        workload=gi.CONFIGS[4]["name"], bytes=nb, flops=fl,
+        workload=gi.WORKLOADS[4]["name"], bytes=nb, flops=fl,
         tokens_per_s=case.B * case.T / sec,
         achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
         achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
@@ -277,7 +312,7 @@ def bench_prefill(torch, lib, steps, warmup):
 def cpu_baseline(budget_s: float = 10.0):
     import gdn_inputs as gi
     import oracle
-    case = gi.config_case(1)
+    case = gi.workload_case(1)
     args = [case.f64(n) for n in ("q", "k", "v", "g", "beta")]
     st = case.f64("state")
     oracle.forward(*args, st)  # load / build
@@ -300,6 +335,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 20 device copies of 64 MiB (a plain copy kernel of known "
+                         "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--only", choices=["decode", "verify", "prefill", "all"], default="all",
                     help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
@@ -325,6 +363,14 @@ def main():
         dec = bench_decode(torch, lib, args.steps, args.warmup)
         log(f"decode: {dec['us_per_launch']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s "
             f"(eager {dec['eager_us_per_launch']:.2f} us)")
+    if args.copy_calibration:
+        log("copy calibration: 20 x 64 MiB device copies ...")
+        src = torch.randn(16 * 1024 * 1024, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     paths = {}
     if args.only in ("verify", "all"):
         for cfg in (2, 3):
@@ -374,7 +420,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": dec["achieved_gbs"] / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": decode_traffic_bytes(),
             "kernel": "gdn::recurrent_kernel<128, GDA, bf16, single token>",
             "bytes_per_launch": dec["bytes"],
             "us_per_launch": dec["us_per_launch"],

@@ -41,8 +41,8 @@ __all__ = [
     "bf16_round",
     "bf16_bits",
     "bf16_from_bits",
-    "CONFIGS",
-    "config_case",
+    "WORKLOADS",
+    "workload_case",
 ]
 
 
@@ -161,8 +161,8 @@ def make_case(
                 state, accepted)
 
 
-# The five synthetic workloads: (name, kwargs for make_case, seed).
-CONFIGS = {
+# The five synthetic workloads (name and make_case arguments; the seed is the index).
+WORKLOADS = {
     0: dict(name="tiny GDA B=1 H=2 d=64 T=16 fp32 K=1",
             B=1, T=16, H=2, d_k=64, K=1, gate="gda", qkv_dtype="f32"),
     1: dict(name="decode GDA B=64 H=16 d=128 T=1",
@@ -179,9 +179,9 @@ CONFIGS = {
 }
 
 
-def config_case(i: int, seed: int | None = None, **override) -> Case:
-    """Case for workload ``i`` (seed defaults to the workload index)."""
-    kw = dict(CONFIGS[i])
+def workload_case(i: int, seed: int | None = None, **override) -> Case:
+    """Case for workload ``i`` of WORKLOADS (seed defaults to the workload index)."""
+    kw = dict(WORKLOADS[i])
     kw.pop("name")
     kw.update(override)
     return make_case(seed=i if seed is None else seed, **kw)

@@ -44,6 +44,9 @@
 #ifndef GDN_DEC_NT_LOAD
 #define GDN_DEC_NT_LOAD 1
 #endif
+#ifndef GDN_DEC_NT_STORE
+#define GDN_DEC_NT_STORE 1
+#endif
 
 namespace gdn {
 
@@ -61,6 +64,14 @@ __device__ __forceinline__ f32x4 load_state(const float* p) {
     return ld4_nt(p);
 #else
     return ld4(p);
+#endif
+}
+
+__device__ __forceinline__ void store_state(float* p, f32x4 v) {
+#if GDN_DEC_NT_STORE
+    st4_nt(p, v);
+#else
+    st4(p, v);
 #endif
 }
 
@@ -272,19 +283,19 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         if (!ONE && t < n_snap) {
             float* dst = slots + static_cast<size_t>(t + 1) * TILE;
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) st4_nt(dst + static_cast<size_t>(row0 + i) * D + col0, s[i]);
+            for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * D + col0, s[i]);
         }
         if (!ONE) cur = nxt;
     }
 
     if (K == 1) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) st4_nt(slots + static_cast<size_t>(row0 + i) * D + col0, s[i]);
+        for (int i = 0; i < RPL; ++i) store_state(slots + static_cast<size_t>(row0 + i) * D + col0, s[i]);
     }
     if (final_state != nullptr) {
         float* dst = final_state + static_cast<size_t>(bh) * TILE;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) st4_nt(dst + static_cast<size_t>(row0 + i) * D + col0, s[i]);
+        for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * D + col0, s[i]);
     }
 }
 

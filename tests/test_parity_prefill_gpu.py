@@ -50,7 +50,7 @@ def _check(case, o, s, tol=TOL):
 
 
 def test_prefill_workload_full_size():
-    c = gi.config_case(4)
+    c = gi.workload_case(4)
     o, s, _ = _prefill(c)
     _check(c, o, s)
 

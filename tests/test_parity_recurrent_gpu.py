@@ -67,13 +67,13 @@ def _check_against_oracle(case, o, st, fin):
 
 
 def test_config0_tiny_fp32():
-    c = gi.config_case(0)
+    c = gi.workload_case(0)
     o, st, fin = _run_snapshots(c)
     _check_against_oracle(c, o, st, fin)
 
 
 def test_config1_decode_full_size():
-    c = gi.config_case(1)
+    c = gi.workload_case(1)
     d = upload(c)
     state = d["state"][:, :, 0].contiguous()  # [B,H,d,d], K = 1
     o = _gdn().gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
@@ -86,7 +86,7 @@ def test_config1_decode_full_size():
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_verify_and_rollback_full_size(cfg):
-    c = gi.config_case(cfg)
+    c = gi.workload_case(cfg)
     d = upload(c)
     fin = torch.empty((c.B, c.H, c.d_k, c.d_v), device="cuda")
     o = _gdn().gdn_forward_snapshots(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], fin)
@@ -168,7 +168,7 @@ def test_zero_tokens_copies_final_state_only():
 
 
 def test_repeat_runs_bitwise_deterministic():
-    c = gi.config_case(2)
+    c = gi.workload_case(2)
     outs = []
     for _ in range(2):
         o, st, fin = _run_snapshots(c)
