@@ -193,7 +193,10 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
     }
 
-    // QKm = lower part (diagonal included) of exp(G_r - G_s) o (Q K^T), as hi/lo
+    // QKm = lower part (diagonal included) of exp(G_r - G_s) o (Q K^T), as
+    // hi/lo.  Each 16 x 16 tile is formed transposed (K Q^T), so a lane holds
+    // 4 consecutive columns s of one row r and stores them with one 8-byte
+    // write per array.
     {
         bf16x8 qf[4][KS];
 #pragma unroll
@@ -206,32 +209,25 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         uint16_t* qkh = reinterpret_cast<uint16_t*>(wsb + kWsQkHi);
         uint16_t* qkl = reinterpret_cast<uint16_t*>(wsb + kWsQkLo);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int rt = 0; rt < 4; ++rt) {  // tile of rows r (the query index)
+            const int r = 16 * rt + lr;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int col = 16 * nt + lr;
-                if (nt > mt) {
+            for (int st = 0; st < 4; ++st) {  // tile of columns s (the key index)
+                const int s0 = 16 * st + 4 * grp;
+                u32x2 hi = {0u, 0u}, lo = {0u, 0u};
+                if (st <= rt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int row = 16 * mt + 4 * grp + rr;
-                        qkh[row * kC + col] = 0;
-                        qkl[row * kC + col] = 0;
-                    }
-                    continue;
+                    for (int ks = 0; ks < KS; ++ks) acc = mfma(kf[st][ks], qf[rt][ks], acc);
+                    // acc[j] = q_r . k_(s0 + j)
+                    float x[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        x[j] = (s0 + j <= r) ? expf(sG[r] - sG[s0 + j]) * acc[j] : 0.f;
+                    split4(x[0], x[1], x[2], x[3], hi, lo);
                 }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma(qf[mt][ks], kf[nt][ks], acc);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int row = 16 * mt + 4 * grp + rr;
-                    float x = 0.f;
-                    if (col <= row) x = expf(sG[row] - sG[col]) * acc[rr];
-                    uint32_t hi, lo;
-                    split_bf16(x, hi, lo);
-                    qkh[row * kC + col] = static_cast<uint16_t>(hi);
-                    qkl[row * kC + col] = static_cast<uint16_t>(lo);
-                }
+                *reinterpret_cast<u32x2*>(qkh + r * kC + s0) = hi;
+                *reinterpret_cast<u32x2*>(qkl + r * kC + s0) = lo;
             }
         }
     }
@@ -250,11 +246,11 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int s4 = 0; s4 < 16 * I; s4 += 4) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[16 * I + i][s4]);
-                y[i] = fmaf(-a.x, x[s4], y[i]);
-                y[i] = fmaf(-a.y, x[s4 + 1], y[i]);
-                y[i] = fmaf(-a.z, x[s4 + 2], y[i]);
-                y[i] = fmaf(-a.w, x[s4 + 3], y[i]);
+                const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * I + i][s4]);
+                y[i] = fmaf(-av.x, x[s4], y[i]);
+                y[i] = fmaf(-av.y, x[s4 + 1], y[i]);
+                y[i] = fmaf(-av.z, x[s4 + 2], y[i]);
+                y[i] = fmaf(-av.w, x[s4 + 3], y[i]);
             }
         }
 #pragma unroll
@@ -265,16 +261,28 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             x[16 * I + i] = acc;
         }
     }
-    // T1 = T diag(beta): scale this lane's column, store as hi/lo bf16
-    uint16_t* t1h = reinterpret_cast<uint16_t*>(wsb + kWsT1Hi);
-    uint16_t* t1l = reinterpret_cast<uint16_t*>(wsb + kWsT1Lo);
+
+    // T1 = T diag(beta): this lane's column, split hi/lo, transposed through
+    // LDS (the A matrix is no longer read) so the stores are 16 bytes wide.
+    __syncthreads();  // every read of A is done before its storage is reused
+    uint16_t (*sT)[kC][kC] = reinterpret_cast<uint16_t (*)[kC][kC]>(&sA[0][0]);
     const float bcol = sBeta[lane];
 #pragma unroll
     for (int r = 0; r < kC; ++r) {
         uint32_t hi, lo;
         split_bf16(x[r] * bcol, hi, lo);
-        t1h[r * kC + lane] = static_cast<uint16_t>(hi);
-        t1l[r * kC + lane] = static_cast<uint16_t>(lo);
+        sT[0][r][lane] = static_cast<uint16_t>(hi);
+        sT[1][r][lane] = static_cast<uint16_t>(lo);
+    }
+    __syncthreads();
+    uint16_t* t1h = reinterpret_cast<uint16_t*>(wsb + kWsT1Hi);
+    uint16_t* t1l = reinterpret_cast<uint16_t*>(wsb + kWsT1Lo);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int piece = lane + 64 * i;  // 64 rows x 8 pieces of 16 bytes
+        const int r = piece >> 3, c = 8 * (piece & 7);
+        *reinterpret_cast<u32x4*>(t1h + r * kC + c) = *reinterpret_cast<const u32x4*>(&sT[0][r][c]);
+        *reinterpret_cast<u32x4*>(t1l + r * kC + c) = *reinterpret_cast<const u32x4*>(&sT[1][r][c]);
     }
 }
 
@@ -320,8 +328,20 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int wave = tid >> 6;
     const int lr = lane & 15;
     const int grp = lane >> 4;
-    const int cb = blockIdx.x % NCB;
-    const int bh = blockIdx.x / NCB;
+    // Workgroups are dispatched to the 8 XCDs in turn (workgroup i on XCD
+    // i % 8), and each XCD has its own L2.  All column blocks of a head read
+    // the same per-chunk operands, so they are placed on one XCD: with the
+    // head count a multiple of 8, workgroup i runs head (i % 8) + 8 * (j / NCB)
+    // and column block j % NCB, where j = i / 8.
+    int cb, bh;
+    if (((gridDim.x / NCB) & 7) == 0) {
+        const int j = blockIdx.x >> 3;
+        bh = (blockIdx.x & 7) + 8 * (j / NCB);
+        cb = j % NCB;
+    } else {
+        cb = blockIdx.x % NCB;
+        bh = blockIdx.x / NCB;
+    }
     const int b = bh / H;
     const int h = bh - b * H;
     const int col = cb * 16 + lr;
@@ -442,7 +462,6 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     auto step = [&](int n, const Ops& cur, Ops& nxt) {
         const int buf = n & 1;
         __syncthreads();  // sK[buf] and sS hold chunk n's K and the chunk start state
-        load_ops(min(n + 1, NC - 1), nxt);  // prefetch (the last chunk reloads itself)
 
         // X = K S and P = Q S for rows 16*wave.. of the chunk
         f32x4 X = {0.f, 0.f, 0.f, 0.f};
@@ -454,6 +473,9 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             X = mfma(aK, bS, X);
             P = mfma(cur.qf[ks], bS, P);
         }
+        // prefetch the next chunk (the last chunk reloads itself) behind the
+        // products on the critical path
+        load_ops(min(n + 1, NC - 1), nxt);
 
         // R = V - exp(G) X  ->  LDS as hi/lo, transposed [col][row]
         {
