@@ -119,6 +119,10 @@ def test_prefill_validation(lib):
     assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, P, small - 1, None) == ERR_WS
     assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, ctypes.c_void_p(272), small, None) == ERR_WS
     assert pf(1, 0, 2, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == OK
+    # one sequence's [T,H,d] fp32 rows must stay below 2^31 bytes
+    huge_T = (1 << 31) // (16 * 128 * 4)
+    assert pf(1, huge_T, 16, 128, 128, 64, P, P, P, P, P, P, P, P, 1 << 40, None) == ERR_UNSUP
+    assert pf(1, huge_T - 1, 16, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == ERR_WS
 
 
 def test_workspace_grows_with_tokens(lib):

@@ -237,3 +237,38 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert np.array_equal(bits(o2), ref_o)
         assert np.array_equal(bits(work2), ref_s)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate", ["gda", "kda"])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_single_token_kernel_all_variants(d, gate, dt):
+    """The single-token decode instantiation for every head size, gate mode
+    and input dtype."""
+    c = gi.make_case(6, 1, 5, d, K=1, gate=gate, qkv_dtype=dt, seed=500 + d)
+    d_ = upload(c)
+    s = d_["state"][:, :, 0].contiguous()
+    o = _gdn().gdn_forward(d_["q"], d_["k"], d_["v"], d_["g"], d_["beta"], s)
+    torch.cuda.synchronize()
+    ro, rst, _ = oracle.forward(*oracle_args(c), c.f64("state"), kda=gate == "kda")
+    assert rel_err(o, ro) <= TOL and rel_err(s, rst[:, :, 0]) <= TOL
+
+
+def test_large_decode_grid_sampled_heads():
+    """B=512 sequences x 16 heads (512 MiB of state, 8x the decode workload);
+    the oracle checks a seeded sample of (sequence, head) pairs one by one."""
+    B, H, d = 512, 16, 128
+    c = gi.make_case(B, 1, H, d, K=1, gate="gda", qkv_dtype="bf16", seed=808)
+    d_ = upload(c)
+    s = d_["state"][:, :, 0].contiguous()
+    o = _gdn().gdn_forward(d_["q"], d_["k"], d_["v"], d_["g"], d_["beta"], s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    picks = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 24), rng.integers(0, H, 24))]
+    picks += [(0, 0), (B - 1, H - 1)]
+    for b, h in picks:
+        one = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1], dtype=np.float64)
+        ro, rst, _ = oracle.forward(one(c.q), one(c.k), one(c.v), one(c.g), one(c.beta),
+                                    np.asarray(c.state[b:b + 1, h:h + 1], dtype=np.float64))
+        assert rel_err(o[b:b + 1, :, h:h + 1], ro) <= TOL, (b, h)
+        assert rel_err(s[b:b + 1, h:h + 1], rst[:, :, 0]) <= TOL, (b, h)
