@@ -16,19 +16,29 @@
 // Two kernels:
 //  prep  (one wavefront per chunk and head, all chunks in parallel): G,
 //        K K^T and Q K^T on MFMA, the gate masks, the unit lower triangular
-//        inverse T by forward substitution in fp32, and T1 and QKm written to
-//        the workspace as bf16 hi + lo pairs (x = hi + lo to ~2^-17).
-//  chain (one workgroup of 4 wavefronts per head and 16 state columns,
-//        serial over chunks): the fp32 state block lives in MFMA accumulators
-//        (wavefront w owns d_k/4 rows); per chunk it forms X = K S and Q S
-//        (S rounded to bf16 as the B operand), R = V - exp(G) X, W = T1 R,
-//        O, and the state update, exchanging R, W and S through LDS.
-//        Products whose rounding would reach the carried state or the
-//        output visibly use hi/lo operand pairs (T1 R, QKm W, K^T W').
-// Matrix layouts of v_mfma_f32_16x16x32_bf16 as used here: A (16 x 32):
-// lane l holds row l%16, k = 8*(l/16) + 0..7; B (32 x 16): lane l holds
-// column l%16, the same k; D (16 x 16 fp32): lane l holds column l%16, rows
-// 4*(l/16) + 0..3.
+//        inverse T by forward substitution in fp32.  It writes Q, T1 and QKm
+//        to the workspace as ready-made MFMA A operands (T1 and QKm as bf16
+//        hi + lo pairs, x = hi + lo to ~2^-17), in the order the chain
+//        kernel reads them, plus the gate factors.
+//  chain (one workgroup of two wavefronts per head and 16 state columns,
+//        serial over chunks):
+//        the state wavefront keeps the d_k x 16 fp32 state block in MFMA
+//        accumulators and per chunk forms X = K S, R = V - exp(G) X,
+//        W = T1 R and S <- exp(G_last) S + K^T (exp(G_last - G) W); each
+//        product's result feeds the next product from registers;
+//        the output wavefront runs one chunk behind and forms
+//        O = exp(G) Q S + QKm W from the chunk start state and W that the
+//        state wavefront leaves in LDS.  The two meet at one barrier per chunk.
+//        Products whose rounding would reach the carried state or the output
+//        visibly use hi/lo operand pairs (T1 R, QKm W, K^T W').
+//
+// Matrix layouts of v_mfma_f32_16x16x32_bf16: A (16 x 32): lane l holds row
+// l%16, k = 8*(l/16) + 0..7; B (32 x 16): lane l holds column l%16, the same
+// k; D (16 x 16 fp32): lane l holds column l%16, rows 4*(l/16) + 0..3.  The
+// order of k inside one instruction is free as long as A and B agree, so two
+// D tiles stacked along k form a B operand as they are when A is read in the
+// "split" k order {4*(l/16) + 0..3, 16 + 4*(l/16) + 0..3}.  Every product
+// whose B operand is an earlier result uses that order.
 
 #include "device_common.hpp"
 #include "gdn_internal.hpp"
@@ -42,24 +52,41 @@ constexpr int kC = 64;  // chunk length
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Workspace: one block per (sequence, head, chunk): T1 and QKm as bf16 hi/lo
-// (row-major 64 x 64) and the gate factors exp(G_r), exp(G_last - G_r) and
-// exp(G_last) in fp32.
-constexpr int kWsT1Hi = 0;
-constexpr int kWsT1Lo = kC * kC * 2;
-constexpr int kWsQkHi = 2 * kC * kC * 2;
-constexpr int kWsQkLo = 3 * kC * kC * 2;
-constexpr int kWsEG = 4 * kC * kC * 2;     // exp(G_r)
-constexpr int kWsER = kWsEG + kC * 4;      // exp(G_last - G_r)
-constexpr int kWsEL = kWsER + kC * 4;      // exp(G_last)
-constexpr int kWsBlock = kWsEL + 256;      // 33536 bytes, a multiple of 256
+// Workspace: one block per (sequence, head, chunk), written by the prep
+// kernel in the order the chain kernel reads it, so that each chain load
+// instruction reads 1 KiB of contiguous memory:
+//   QF   Q as A operands, [row tile 4][k-step D/32][lane 64][8 bf16] (plain k order)
+//   T1F  T1 as A operands, [row tile 4][k-step 2][hi, lo][lane 64][8 bf16] (split k order)
+//   QKF  the decay-masked Q K^T as A operands, same shape and order as T1F
+//   E    exp(G_r) [64 fp32], exp(G_last - G_r) [64 fp32], exp(G_last), padding to 1 KiB
+template <int D>
+struct Ws {
+    static constexpr int KS = D / 32;  // MFMA k-steps over d_k
+    static constexpr int kQF = 0;
+    static constexpr int kT1F = kQF + 4 * KS * 64 * 16;
+    static constexpr int kQKF = kT1F + 4 * 2 * 2 * 64 * 16;
+    static constexpr int kE = kQKF + 4 * 2 * 2 * 64 * 16;
+    static constexpr int kBlock = kE + 1024;
+    static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
+};
+
+// Byte offset of A operand (row tile t, k-step ks, hi/lo hl) of lane `lane` in T1F / QKF.
+__host__ __device__ constexpr int frag_off(int t, int ks, int hl, int lane) {
+    return (((t * 2 + ks) * 2 + hl) * 64 + lane) * 16;
+}
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two 4-value halves (k = 4g + 0..3 and 16 + 4g + 0..3) -> one split-order operand.
+__device__ __forceinline__ bf16x8 join(const u32x2& lo, const u32x2& hi) {
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
 
 __device__ __forceinline__ bf16x8 ld16_bf16(const void* p) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
@@ -78,10 +105,6 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
     hi = bf16_rne(x);
     lo = bf16_rne(x - __uint_as_float(hi << 16));
-}
-
-__device__ __forceinline__ u32x2 pack4(const uint32_t (&h)[4]) {
-    return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -104,13 +127,50 @@ __device__ __forceinline__ void split4(float a, float b, float c, float d, u32x2
                     c - __uint_as_float(hi[1] << 16), d - __uint_as_float(hi[1] & 0xffff0000u));
 }
 
+__device__ __forceinline__ void split4(const f32x4& x, u32x2& hi, u32x2& lo) {
+    split4(x[0], x[1], x[2], x[3], hi, lo);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zeros (the hardware range check), which handles the rows after the end of a
+// sequence without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes > 0 ? bytes : 0,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Workgroup barrier for data written to LDS with ds_write: waits for this
+// wavefront's LDS operations only, so that outstanding global and
+// direct-to-LDS loads (the prefetch of later chunks, read only by the
+// wavefront that issued them) stay in flight across it.  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait for all of this wavefront's outstanding global and direct-to-LDS
+// loads (s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained; the compiler
+// sees the wait and counts from it).
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Transposing LDS read (ds_read_tr16_b64): within each 16-lane group, lane
+// i receives element i%4 of the 8-byte words that lanes 4j + i/4 point at,
+// j = 0..3.
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p)));
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int B, int T, int H, int d) {
-    (void)d;
-    size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
-    nc += nc & 1;  // an even chunk count (see launch_prefill_t)
-    return static_cast<size_t>(B) * H * nc * kWsBlock;
+    const size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
+    const size_t block = d == 128 ? Ws<128>::kBlock : Ws<64>::kBlock;
+    return static_cast<size_t>(B) * H * nc * block;
 }
 
 // ---------------------------------------------------------------------------
@@ -121,10 +181,18 @@ __global__ void __launch_bounds__(64)
 prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const float* __restrict__ g, const float* __restrict__ beta,
                     char* __restrict__ ws, int T, int H, int NC) {
-    constexpr int KS = D / 32;  // MFMA k-steps over d_k
+    using L = Ws<D>;
+    constexpr int KS = L::KS;
+    // A (fp32) during the solve, then the hi/lo transpose of T1 (bf16); a
+    // barrier separates the two uses.
     __shared__ __attribute__((aligned(16))) float sA[kC][kC];
     __shared__ float sG[kC];
     __shared__ float sBeta[kC];
+    uint16_t (*sT)[kC][kC] = reinterpret_cast<uint16_t (*)[kC][kC]>(&sA[0][0]);
+    // 8-byte unit u of row r of the transpose is kept at unit u ^ tsw(r), so
+    // that the split-order reads below (16 rows, two units each) meet every
+    // bank once.
+    auto tsw = [](int r) { return 2 * ((r >> 1) & 7); };
 
     const int lane = threadIdx.x;
     const int blk = blockIdx.x;  // (b * H + h) * NC + n
@@ -136,6 +204,7 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int nvalid = min(kC, T - t0);
     const int lr = lane & 15;  // MFMA row / column inside a tile
     const int grp = lane >> 4;
+    char* wsb = ws + static_cast<size_t>(blk) * L::kBlock;
 
     // gates: inclusive prefix sum of the log-gates over the chunk
     float gv = 0.f, bv = 0.f;
@@ -152,15 +221,15 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     sG[lane] = G;
     sBeta[lane] = bv;
-    char* wsb = ws + static_cast<size_t>(blk) * kWsBlock;
     {
+        float* e = reinterpret_cast<float*>(wsb + L::kE);
         const float Glast = __shfl(G, 63, 64);
-        reinterpret_cast<float*>(wsb + kWsEG)[lane] = expf(G);
-        reinterpret_cast<float*>(wsb + kWsER)[lane] = expf(Glast - G);
-        if (lane == 0) reinterpret_cast<float*>(wsb + kWsEL)[0] = expf(Glast);
+        e[lane] = expf(G);
+        e[64 + lane] = expf(Glast - G);
+        if (lane == 0) e[128] = expf(Glast);
     }
 
-    // fragments of the chunk's k rows (zero beyond the sequence end)
+    // fragments of the chunk's q and k rows (zero beyond the sequence end)
     auto row_ptr = [&](const uint16_t* base, int r) {
         return base + ((static_cast<size_t>(b) * T + t0 + r) * H + h) * D;
     };
@@ -194,41 +263,50 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     // QKm = lower part (diagonal included) of exp(G_r - G_s) o (Q K^T), as
-    // hi/lo.  Each 16 x 16 tile is formed transposed (K Q^T), so a lane holds
-    // 4 consecutive columns s of one row r and stores them with one 8-byte
-    // write per array.
-    {
-        bf16x8 qf[4][KS];
+    // hi/lo A operands in split k order.  Each 16 x 16 tile is formed
+    // transposed (K Q^T), so lane l holds row r = 16 rt + l%16 and the four
+    // columns s = 16 st + 4 (l/16) + 0..3: the tiles st = 2 ks and 2 ks + 1
+    // give exactly the 8 values of k-step ks in split order.
+    bf16x8 qf[4][KS];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = 16 * t + lr;
+    for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + lr;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[t][ks] = r < nvalid ? ld16_bf16(row_ptr(q, r) + 32 * ks + 8 * grp) : zero_bf16x8();
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[t][ks] = r < nvalid ? ld16_bf16(row_ptr(q, r) + 32 * ks + 8 * grp) : zero_bf16x8();
+            // a q fragment is already the chain's A operand
+            *reinterpret_cast<u32x4*>(wsb + L::kQF + ((t * KS + ks) * 64 + lane) * 16) =
+                __builtin_bit_cast(u32x4, qf[t][ks]);
         }
-        uint16_t* qkh = reinterpret_cast<uint16_t*>(wsb + kWsQkHi);
-        uint16_t* qkl = reinterpret_cast<uint16_t*>(wsb + kWsQkLo);
+    }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {  // tile of rows r (the query index)
-            const int r = 16 * rt + lr;
+    for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + lr;
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {  // tile of columns s (the key index)
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x2 hi[2], lo[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int st = 2 * ks + half;
                 const int s0 = 16 * st + 4 * grp;
-                u32x2 hi = {0u, 0u}, lo = {0u, 0u};
+                hi[half] = u32x2{0u, 0u};
+                lo[half] = u32x2{0u, 0u};
                 if (st <= rt) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) acc = mfma(kf[st][ks], qf[rt][ks], acc);
+                    for (int kk = 0; kk < KS; ++kk) acc = mfma(kf[st][kk], qf[rt][kk], acc);
                     // acc[j] = q_r . k_(s0 + j)
                     float x[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         x[j] = (s0 + j <= r) ? expf(sG[r] - sG[s0 + j]) * acc[j] : 0.f;
-                    split4(x[0], x[1], x[2], x[3], hi, lo);
+                    split4(x[0], x[1], x[2], x[3], hi[half], lo[half]);
                 }
-                *reinterpret_cast<u32x2*>(qkh + r * kC + s0) = hi;
-                *reinterpret_cast<u32x2*>(qkl + r * kC + s0) = lo;
             }
+            *reinterpret_cast<u32x4*>(wsb + L::kQKF + frag_off(rt, ks, 0, lane)) =
+                u32x4{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+            *reinterpret_cast<u32x4*>(wsb + L::kQKF + frag_off(rt, ks, 1, lane)) =
+                u32x4{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
         }
     }
     __syncthreads();
@@ -263,69 +341,106 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     // T1 = T diag(beta): this lane's column, split hi/lo, transposed through
-    // LDS (the A matrix is no longer read) so the stores are 16 bytes wide.
+    // LDS (A is no longer read) into split-order A operands.
     __syncthreads();  // every read of A is done before its storage is reused
-    uint16_t (*sT)[kC][kC] = reinterpret_cast<uint16_t (*)[kC][kC]>(&sA[0][0]);
     const float bcol = sBeta[lane];
 #pragma unroll
     for (int r = 0; r < kC; ++r) {
         uint32_t hi, lo;
         split_bf16(x[r] * bcol, hi, lo);
-        sT[0][r][lane] = static_cast<uint16_t>(hi);
-        sT[1][r][lane] = static_cast<uint16_t>(lo);
+        const int c = 4 * ((lane >> 2) ^ tsw(r)) + (lane & 3);
+        sT[0][r][c] = static_cast<uint16_t>(hi);
+        sT[1][r][c] = static_cast<uint16_t>(lo);
     }
     __syncthreads();
-    uint16_t* t1h = reinterpret_cast<uint16_t*>(wsb + kWsT1Hi);
-    uint16_t* t1l = reinterpret_cast<uint16_t*>(wsb + kWsT1Lo);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int piece = lane + 64 * i;  // 64 rows x 8 pieces of 16 bytes
-        const int r = piece >> 3, c = 8 * (piece & 7);
-        *reinterpret_cast<u32x4*>(t1h + r * kC + c) = *reinterpret_cast<const u32x4*>(&sT[0][r][c]);
-        *reinterpret_cast<u32x4*>(t1l + r * kC + c) = *reinterpret_cast<const u32x4*>(&sT[1][r][c]);
-    }
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const int r = 16 * t + lr;
+                const int u = 8 * ks + grp;  // 8-byte unit of columns 32 ks + 4 grp + 0..3
+                const u32x2 a = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * (u ^ tsw(r))]);
+                const u32x2 c = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * ((u + 4) ^ tsw(r))]);
+                *reinterpret_cast<u32x4*>(wsb + L::kT1F + frag_off(t, ks, hl, lane)) =
+                    u32x4{a[0], a[1], c[0], c[1]};
+            }
 }
 
 // ---------------------------------------------------------------------------
-// chain: one workgroup (4 wavefronts) per (sequence, head, 16-column block)
+// chain: one workgroup (two wavefronts) per (sequence, head, 16-column block)
 // ---------------------------------------------------------------------------
 
-// Raw buffer resource over [base, base + bytes): loads past the end return
-// zeros and stores past the end are dropped (the hardware range check), which
-// handles the rows after the end of a sequence without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes > 0 ? bytes : 0,
-                                             0x00020000);
+// LDS image of a K chunk: row-major [64][D] bf16 with the 16-byte pieces of
+// row r permuted by an XOR with sw(r), so that both the row reads of the
+// X = K S operand (16 rows, one piece each) and the transposing reads of the
+// K^T operand (8 rows, two adjacent pieces each) touch every bank once.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+// Element offset of (r, c) in the K image, c a multiple of 4.
+template <int D>
+__device__ __forceinline__ int k_at(int r, int c) {
+    return r * D + 8 * ((c >> 3) ^ k_swz<D>(r)) + (c & 7);
 }
 
-__device__ __forceinline__ bf16x8 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
-    return as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)));
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// lds + 16 l (lds must be the same for the whole wavefront).  Loads past the
+// end of the resource write zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                             0, 0, 0);
 }
+
+// LDS layout of the chain kernel.  Two slots hold the operands of two
+// consecutive chunks: the workspace block as it is (Q, T1, QKm, gates), the
+// K image and the workgroup's V block.  Loader wavefronts fill one slot while
+// the others compute on the other.
+template <int D>
+struct ChainLds {
+    static constexpr int kWs = 0;                          // workspace block (Ws<D> layout)
+    static constexpr int kK = Ws<D>::kBlock;               // K image (k_at layout)
+    static constexpr int kV = kK + kC * D * 2;             // V block, [64][16] bf16
+    static constexpr int kSlot = kV + kC * 16 * 2;
+    static constexpr int kWsPieces = Ws<D>::kBlock / 1024; // 1 KiB loads per workspace block
+};
+
+constexpr int kStateWaves = 4;   // chunk rows 16 w.., state rows (d_k / 4) w..
+constexpr int kOutWaves = 4;     // chunk rows 16 w.. of the output
+constexpr int kLoadWaves = 3;
+constexpr int kChainThreads = 64 * (kStateWaves + kOutWaves + kLoadWaves);
 
 template <int D>
-__global__ void __launch_bounds__(256)
-prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                     const uint16_t* __restrict__ v, float* __restrict__ state,
-                     float* __restrict__ o, const char* __restrict__ ws, int T, int H, int NC) {
-    constexpr int NCB = D / 16;     // column blocks per head
-    constexpr int KS = D / 32;      // k-steps over d_k
-    constexpr int SROWS = D / 4;    // state rows per wavefront
-    constexpr int SMT = SROWS / 16; // state tiles per wavefront
-    constexpr int KLD = D + 8;      // padded LDS row of the K chunk (bf16)
-    constexpr int CLD = kC + 8;     // padded LDS row of the [col][chunk row] buffers
-    constexpr int SLD = D + 8;      // padded LDS row of S^T
-    constexpr int KPT = kC * D / 8 / 256;  // 16-byte K pieces per thread
+__global__ void __launch_bounds__(kChainThreads)
+prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                     float* __restrict__ state, float* __restrict__ o,
+                     const char* __restrict__ ws, int T, int H, int NC) {
+    using L = Ws<D>;
+    using M = ChainLds<D>;
+    constexpr int NCB = D / 16;        // column blocks per head
+    constexpr int KS = L::KS;          // k-steps over d_k
+    constexpr int SRW = D / 4;         // state rows per state wavefront
+    constexpr int SMT = SRW / 16;      // state tiles per state wavefront
+    constexpr int PPR = D / 8;         // 16-byte pieces per K row
+    constexpr int KPT = kC * PPR / 64; // 1 KiB loads of the K image
+    constexpr int SLD = D + 8;         // padded row of sS (bf16)
+    constexpr int CLD = kC + 8;        // padded row of sR, sW, sWp (bf16)
+    constexpr int OLD = 20;            // padded row of sO (fp32)
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kC][KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sS[16][SLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sR[2][16][CLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sW[2][16][CLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sWp[2][16][CLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][16][CLD];  // V block, [col][row]
+    __shared__ __attribute__((aligned(16))) char sL[2][M::kSlot];
+    __shared__ __attribute__((aligned(16))) uint16_t sS[16][SLD];       // chunk start state, [col][d_k]
+    __shared__ __attribute__((aligned(16))) uint16_t sR[2][16][CLD];    // R hi/lo, [col][chunk row]
+    __shared__ __attribute__((aligned(16))) uint16_t sW[2][16][CLD];    // W hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sWp[2][16][CLD];   // W' = exp(G_last - G) W hi/lo
+    __shared__ __attribute__((aligned(16))) float sO[kC][OLD];           // the chunk's output block
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    // the role of a wavefront is uniform across it: keep it in a scalar
+    // register so that the roles are separate branches of the program
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15;
     const int grp = lane >> 4;
     // Workgroups are dispatched to the 8 XCDs in turn (workgroup i on XCD
@@ -346,237 +461,224 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int h = bh - b * H;
     const int col = cb * 16 + lr;
 
-    // per (sequence, head) views; a token row is H*D elements apart
-    const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;  // element of (b, t=0, h, 0)
-    const int row_b16 = H * D * 2;                                  // bytes per token, bf16
-    const int seq_b16 = (T - 1) * row_b16 + D * 2;  // bytes of the last valid row's end
-
-    // per-lane byte offsets inside a chunk (constant over the chunks)
-    int koff[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int piece = tid + 256 * i;
-        koff[i] = (piece / (D / 8)) * row_b16 + (piece % (D / 8)) * 16;
-    }
-    const int ra = 16 * wave + lr;  // A-operand row of this lane
-    const int qoff = ra * row_b16 + 16 * grp;
-    const int woff = (ra * kC + 8 * grp) * 2;
-    // V block of the chunk (64 rows x 16 columns): one 8-byte piece per thread
-    const int vrow = tid >> 2, vq = tid & 3;
-    const int voff = vrow * row_b16 + (cb * 16 + 4 * vq) * 2;
-    const int goff = (16 * wave + 4 * grp) * 4;  // this lane's rows in the gate-factor arrays
-    float* const obase = o + head0 + static_cast<size_t>(16 * wave + 4 * grp) * H * D + col;
-
-    // ---- initial state block (fp32, accumulator layout) --------------------
-    float* st = state + static_cast<size_t>(bh) * D * D;
-    f32x4 S[SMT];
-#pragma unroll
-    for (int mt = 0; mt < SMT; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            S[mt][rr] = st[static_cast<size_t>(wave * SROWS + 16 * mt + 4 * grp + rr) * D + col];
-
-    auto write_state_lds = [&]() {
+    if (wave < kStateWaves) {
+        // ======================= state wavefronts ==========================
+        const int w = wave;
+        float* st = state + static_cast<size_t>(bh) * D * D;
+        // tile mt: d_k rows SRW w + 16 mt + 4 grp + 0..3 of column `col`
+        f32x4 S[SMT];
 #pragma unroll
         for (int mt = 0; mt < SMT; ++mt)
-            *reinterpret_cast<u32x2*>(&sS[lr][wave * SROWS + 16 * mt + 4 * grp]) =
-                to_bf16x4(S[mt][0], S[mt][1], S[mt][2], S[mt][3]);
-    };
-
-    // ---- per-chunk operands held in registers ------------------------------
-    struct Ops {
-        u32x4 kpiece[KPT];     // K chunk pieces, staged to LDS
-        bf16x8 qf[KS];         // Q rows 16*wave.. (A operand)
-        bf16x8 t1h[2], t1l[2]; // T1 rows 16*wave.. hi/lo
-        bf16x8 qkh[2], qkl[2]; // QKm rows 16*wave.. hi/lo
-        u32x2 vpiece;          // 4 bf16 of V, staged to LDS
-        f32x4 eg;              // exp(G) at rows 16*wave + 4*grp + 0..3
-        f32x4 er;              // exp(G_last - G) at the same rows
-        float el;              // exp(G_last)
-    };
-
-    // Loads of chunk n's operands: buffer loads with constant per-lane
-    // offsets from per-chunk (scalar) resources; rows past the sequence end
-    // come back as zeros.
-    auto load_ops = [&](int n, Ops& p) {
-        const int cbyte = n * kC;  // first token of the chunk
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head0 + static_cast<size_t>(cbyte) * H * D,
-                                                     seq_b16 - cbyte * row_b16);
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head0 + static_cast<size_t>(cbyte) * H * D,
-                                                     seq_b16 - cbyte * row_b16);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head0 + static_cast<size_t>(cbyte) * H * D,
-                                                     seq_b16 - cbyte * row_b16);
-        const __amdgpu_buffer_rsrc_t rw =
-            make_rsrc(ws + (static_cast<size_t>(bh) * NC + n) * kWsBlock, kWsBlock);
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            p.kpiece[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0));
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) p.qf[ks] = buf_ld16(rq, qoff + 64 * ks);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            p.t1h[ks] = buf_ld16(rw, kWsT1Hi + woff + 64 * ks);
-            p.t1l[ks] = buf_ld16(rw, kWsT1Lo + woff + 64 * ks);
-            p.qkh[ks] = buf_ld16(rw, kWsQkHi + woff + 64 * ks);
-            p.qkl[ks] = buf_ld16(rw, kWsQkLo + woff + 64 * ks);
-        }
-        p.vpiece = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0));
-        p.eg = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kWsEG + goff, 0, 0));
-        p.er = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kWsER + goff, 0, 0));
-        // uniform address: a scalar load
-        p.el = *reinterpret_cast<const float*>(ws + (static_cast<size_t>(bh) * NC + n) * kWsBlock + kWsEL);
-    };
-
-    auto stage_k = [&](const Ops& p, int buf) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int piece = tid + 256 * i;
-            const int r = piece / (D / 8);
-            const int c8 = piece % (D / 8);
-            *reinterpret_cast<u32x4*>(&sK[buf][r][8 * c8]) = p.kpiece[i];
-        }
-        sV[buf][4 * vq + 0][vrow] = static_cast<uint16_t>(p.vpiece[0]);
-        sV[buf][4 * vq + 1][vrow] = static_cast<uint16_t>(p.vpiece[0] >> 16);
-        sV[buf][4 * vq + 2][vrow] = static_cast<uint16_t>(p.vpiece[1]);
-        sV[buf][4 * vq + 3][vrow] = static_cast<uint16_t>(p.vpiece[1] >> 16);
-    };
-
-    // K^T fragment (rows dk0..dk0+15 of d_k, chunk rows 32*ks + 8*grp + 0..7)
-    // from the row-major K chunk with two transposing LDS reads: source lane
-    // s of each 16-lane group points at K[r0 + s/4][dk0 + 4*(s%4)], and lane
-    // i receives K[r0 + j][dk0 + i] for j = 0..3.
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    auto kt_frag = [&](int buf, int dk0, int ks) {
-        const int r0 = 32 * ks + 8 * grp + (lr >> 2);
-        const int c0 = dk0 + 4 * (lr & 3);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(&sK[buf][r0][c0]));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(&sK[buf][r0 + 4][c0]));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        return as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
-    };
-
-    // One chunk: the state chain (X, R, W, S) first, then the outputs.
-    auto step = [&](int n, const Ops& cur, Ops& nxt) {
-        const int buf = n & 1;
-        __syncthreads();  // sK[buf] and sS hold chunk n's K and the chunk start state
-
-        // X = K S and P = Q S for rows 16*wave.. of the chunk
-        f32x4 X = {0.f, 0.f, 0.f, 0.f};
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 bS = ld16_bf16(&sS[lr][32 * ks + 8 * grp]);
-            const bf16x8 aK = ld16_bf16(&sK[buf][16 * wave + lr][32 * ks + 8 * grp]);
-            X = mfma(aK, bS, X);
-            P = mfma(cur.qf[ks], bS, P);
-        }
-        // prefetch the next chunk (the last chunk reloads itself) behind the
-        // products on the critical path
-        load_ops(min(n + 1, NC - 1), nxt);
-
-        // R = V - exp(G) X  ->  LDS as hi/lo, transposed [col][row]
-        {
-            const u32x2 vv = *reinterpret_cast<const u32x2*>(&sV[buf][lr][16 * wave + 4 * grp]);
-            u32x2 rh, rl;
-            split4(__uint_as_float(vv[0] << 16) - cur.eg[0] * X[0],
-                   __uint_as_float(vv[0] & 0xffff0000u) - cur.eg[1] * X[1],
-                   __uint_as_float(vv[1] << 16) - cur.eg[2] * X[2],
-                   __uint_as_float(vv[1] & 0xffff0000u) - cur.eg[3] * X[3], rh, rl);
-            *reinterpret_cast<u32x2*>(&sR[0][lr][16 * wave + 4 * grp]) = rh;
-            *reinterpret_cast<u32x2*>(&sR[1][lr][16 * wave + 4 * grp]) = rl;
-        }
-        __syncthreads();
-
-        // W = T1 R (three hi/lo products)
-        f32x4 W = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 bh_ = ld16_bf16(&sR[0][lr][32 * ks + 8 * grp]);
-            const bf16x8 bl_ = ld16_bf16(&sR[1][lr][32 * ks + 8 * grp]);
-            W = mfma(cur.t1h[ks], bh_, W);
-            W = mfma(cur.t1h[ks], bl_, W);
-            W = mfma(cur.t1l[ks], bh_, W);
-        }
-        {
-            u32x2 wh, wl, ph, pl;
-            split4(W[0], W[1], W[2], W[3], wh, wl);
-            split4(cur.er[0] * W[0], cur.er[1] * W[1], cur.er[2] * W[2], cur.er[3] * W[3], ph, pl);
-            *reinterpret_cast<u32x2*>(&sW[0][lr][16 * wave + 4 * grp]) = wh;
-            *reinterpret_cast<u32x2*>(&sW[1][lr][16 * wave + 4 * grp]) = wl;
-            *reinterpret_cast<u32x2*>(&sWp[0][lr][16 * wave + 4 * grp]) = ph;
-            *reinterpret_cast<u32x2*>(&sWp[1][lr][16 * wave + 4 * grp]) = pl;
-        }
-        __syncthreads();
-
-        // S <- exp(G_last) S + K^T W'
-#pragma unroll
-        for (int mt = 0; mt < SMT; ++mt) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= cur.el;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 aKt = kt_frag(buf, wave * SROWS + 16 * mt, ks);
-                const bf16x8 bh_ = ld16_bf16(&sWp[0][lr][32 * ks + 8 * grp]);
-                const bf16x8 bl_ = ld16_bf16(&sWp[1][lr][32 * ks + 8 * grp]);
-                S[mt] = mfma(aKt, bh_, S[mt]);
-                S[mt] = mfma(aKt, bl_, S[mt]);
-            }
-        }
-        // no wavefront reads sS past the barriers above
-        write_state_lds();
-
-        // O = exp(G) P + QKm W
-        {
-            f32x4 O;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) O[rr] = cur.eg[rr] * P[rr];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 bh_ = ld16_bf16(&sW[0][lr][32 * ks + 8 * grp]);
-                const bf16x8 bl_ = ld16_bf16(&sW[1][lr][32 * ks + 8 * grp]);
-                O = mfma(cur.qkh[ks], bh_, O);
-                O = mfma(cur.qkh[ks], bl_, O);
-                O = mfma(cur.qkl[ks], bh_, O);
-            }
-            // plain global stores (the raw buffer store builtin miscompiles
-            // element extraction from accumulator registers here)
-            const int t0 = n * kC;
-            float* orow = obase + static_cast<size_t>(t0) * H * D;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                if (t0 + 16 * wave + 4 * grp + rr < T) orow[rr * static_cast<size_t>(H) * D] = O[rr];
+                S[mt][rr] = st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * D + col];
+        auto publish_state = [&]() {  // bf16 state rows -> sS (B operand of K S and Q S)
+#pragma unroll
+            for (int mt = 0; mt < SMT; ++mt)
+                *reinterpret_cast<u32x2*>(&sS[lr][SRW * w + 16 * mt + 4 * grp]) =
+                    to_bf16x4(S[mt][0], S[mt][1], S[mt][2], S[mt][3]);
+        };
+        publish_state();
+
+        for (int n = 0; n < NC; ++n) {
+            const char* slot = sL[n & 1];
+            const uint16_t* sK = reinterpret_cast<const uint16_t*>(slot + M::kK);
+            const uint16_t* sV = reinterpret_cast<const uint16_t*>(slot + M::kV);
+            const float* E = reinterpret_cast<const float*>(slot + L::kE);
+            lds_barrier();  // B1: chunk n's operands and start state are in LDS
+
+            // X = K S for chunk rows 16 w + l%16 (plain k order over d_k)
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = ld16_bf16(&sK[k_at<D>(16 * w + lr, 32 * ks + 8 * grp)]);
+                X = mfma(a, ld16_bf16(&sS[lr][32 * ks + 8 * grp]), X);
+            }
+            // R = V - exp(G) X for this wavefront's rows, hi/lo to LDS
+            {
+                const u32x2 vv = ld_tr(&sV[(16 * w + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3)]);
+                const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[16 * w + 4 * grp]);
+                u32x2 rh, rl;
+                split4(__uint_as_float(vv[0] << 16) - eg[0] * X[0],
+                       __uint_as_float(vv[0] & 0xffff0000u) - eg[1] * X[1],
+                       __uint_as_float(vv[1] << 16) - eg[2] * X[2],
+                       __uint_as_float(vv[1] & 0xffff0000u) - eg[3] * X[3], rh, rl);
+                *reinterpret_cast<u32x2*>(&sR[0][lr][16 * w + 4 * grp]) = rh;
+                *reinterpret_cast<u32x2*>(&sR[1][lr][16 * w + 4 * grp]) = rl;
+            }
+            lds_barrier();  // B2: all of R is in LDS
+
+            // W = T1 R for rows 16 w + l%16 (three hi/lo products, split k order)
+            f32x4 W = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int c = 32 * ks + 4 * grp;
+                const bf16x8 th = ld16_bf16(slot + L::kT1F + frag_off(w, ks, 0, lane));
+                const bf16x8 tl = ld16_bf16(slot + L::kT1F + frag_off(w, ks, 1, lane));
+                const bf16x8 rh = join(*reinterpret_cast<const u32x2*>(&sR[0][lr][c]),
+                                       *reinterpret_cast<const u32x2*>(&sR[0][lr][c + 16]));
+                const bf16x8 rl = join(*reinterpret_cast<const u32x2*>(&sR[1][lr][c]),
+                                       *reinterpret_cast<const u32x2*>(&sR[1][lr][c + 16]));
+                W = mfma(th, rh, W);
+                W = mfma(th, rl, W);
+                W = mfma(tl, rh, W);
+            }
+            {
+                const f32x4 er = *reinterpret_cast<const f32x4*>(&E[64 + 16 * w + 4 * grp]);
+                u32x2 wh, wl, ph, pl;
+                split4(W, wh, wl);
+                split4(er[0] * W[0], er[1] * W[1], er[2] * W[2], er[3] * W[3], ph, pl);
+                *reinterpret_cast<u32x2*>(&sW[0][lr][16 * w + 4 * grp]) = wh;
+                *reinterpret_cast<u32x2*>(&sW[1][lr][16 * w + 4 * grp]) = wl;
+                *reinterpret_cast<u32x2*>(&sWp[0][lr][16 * w + 4 * grp]) = ph;
+                *reinterpret_cast<u32x2*>(&sWp[1][lr][16 * w + 4 * grp]) = pl;
+            }
+            lds_barrier();  // B3: all of W and W' are in LDS
+
+            // S <- exp(G_last) S + K^T W' for this wavefront's state rows.
+            // The K^T operand (d_k rows SRW w + 16 mt + l%16, chunk rows in
+            // split order) comes from two transposing reads of the K image.
+            const float el = E[128];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int c = 32 * ks + 4 * grp;
+                const bf16x8 ph = join(*reinterpret_cast<const u32x2*>(&sWp[0][lr][c]),
+                                       *reinterpret_cast<const u32x2*>(&sWp[0][lr][c + 16]));
+                const bf16x8 pl = join(*reinterpret_cast<const u32x2*>(&sWp[1][lr][c]),
+                                       *reinterpret_cast<const u32x2*>(&sWp[1][lr][c + 16]));
+#pragma unroll
+                for (int mt = 0; mt < SMT; ++mt) {
+                    if (ks == 0)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= el;
+                    const int r = 32 * ks + 4 * grp + (lr >> 2);
+                    const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
+                    const bf16x8 a = join(ld_tr(&sK[k_at<D>(r, cc)]), ld_tr(&sK[k_at<D>(r + 16, cc)]));
+                    S[mt] = mfma(a, ph, S[mt]);
+                    S[mt] = mfma(a, pl, S[mt]);
+                }
+            }
+            // sS was last read before B2 (by every wavefront)
+            publish_state();
         }
-        stage_k(nxt, buf ^ 1);  // sK[buf ^ 1] was last read in the previous chunk
-    };
+        lds_barrier();  // the output of the last chunk is in LDS
 
-    // Two operand buffers used in turn (no register copies between chunks).
-    Ops opa, opb;
-    load_ops(0, opa);
-    stage_k(opa, 0);
-    write_state_lds();
-    for (int n = 0; n < NC; n += 2) {  // NC is even
-        step(n, opa, opb);
-        step(n + 1, opb, opa);
+#pragma unroll
+        for (int mt = 0; mt < SMT; ++mt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * D + col] = S[mt][rr];
+        return;
     }
-
+    if (wave < kStateWaves + kOutWaves) {
+        // ====================== output wavefronts ==========================
+        const int w = wave - kStateWaves;
+        for (int n = 0; n < NC; ++n) {
+            const char* slot = sL[n & 1];
+            const float* E = reinterpret_cast<const float*>(slot + L::kE);
+            lds_barrier();  // B1
+            // P = Q S for chunk rows 16 w + l%16
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < SMT; ++mt)
+            for (int ks = 0; ks < KS; ++ks)
+                O = mfma(ld16_bf16(slot + L::kQF + ((w * KS + ks) * 64 + lane) * 16),
+                         ld16_bf16(&sS[lr][32 * ks + 8 * grp]), O);
+            lds_barrier();  // B2
+            lds_barrier();  // B3: W is in LDS
+            // O = exp(G) P + QKm W
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[16 * w + 4 * grp]);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            st[static_cast<size_t>(wave * SROWS + 16 * mt + 4 * grp + rr) * D + col] = S[mt][rr];
+            for (int rr = 0; rr < 4; ++rr) O[rr] *= eg[rr];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int c = 32 * ks + 4 * grp;
+                const bf16x8 wh = join(*reinterpret_cast<const u32x2*>(&sW[0][lr][c]),
+                                       *reinterpret_cast<const u32x2*>(&sW[0][lr][c + 16]));
+                const bf16x8 wl = join(*reinterpret_cast<const u32x2*>(&sW[1][lr][c]),
+                                       *reinterpret_cast<const u32x2*>(&sW[1][lr][c + 16]));
+                const bf16x8 qh = ld16_bf16(slot + L::kQKF + frag_off(w, ks, 0, lane));
+                const bf16x8 ql = ld16_bf16(slot + L::kQKF + frag_off(w, ks, 1, lane));
+                O = mfma(qh, wh, O);
+                O = mfma(qh, wl, O);
+                O = mfma(ql, wh, O);
+            }
+            // to LDS; a loader wavefront stores the block during the next
+            // chunk (the last loader read sO before this chunk's B2)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sO[16 * w + 4 * grp + rr][lr] = O[rr];
+        }
+        lds_barrier();  // the output of the last chunk is in LDS
+        return;
+    }
+    {
+        // ====================== loader wavefronts ==========================
+        // Each fills its share of the next chunk's slot with direct-to-LDS
+        // loads and waits for them before the next chunk's first barrier, so
+        // the other wavefronts read the slot after that barrier.
+        const int l = wave - kStateWaves - kOutWaves;
+        const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;  // element of (b, t=0, h, 0)
+        const int row_b16 = H * D * 2;                                  // bytes per token, bf16
+        const int seq_b16 = (T - 1) * row_b16 + D * 2;  // end of the last valid row
+        const char* wsh = ws + static_cast<size_t>(bh) * NC * L::kBlock;
+        // workspace pieces [lo, hi) for this loader; the last one also loads K and V
+        constexpr int kShare = (M::kWsPieces + KPT + 2 + kLoadWaves - 1) / kLoadWaves;
+        const int lo = min(l * kShare, M::kWsPieces);
+        const int hi = (l == kLoadWaves - 1) ? M::kWsPieces : min(lo + kShare, M::kWsPieces);
+        auto load = [&](int n) {
+            char* slot = sL[n & 1];
+            const __amdgpu_buffer_rsrc_t rw =
+                make_rsrc(wsh + static_cast<size_t>(n) * L::kBlock, L::kBlock);
+            for (int i = lo; i < hi; ++i) dma16(rw, slot + M::kWs + 1024 * i, 1024 * i + 16 * lane);
+            if (l == kLoadWaves - 1) {
+                const int r0 = n * kC;
+                const __amdgpu_buffer_rsrc_t rk =
+                    make_rsrc(k + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+                const __amdgpu_buffer_rsrc_t rv =
+                    make_rsrc(v + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+#pragma unroll
+                for (int i = 0; i < KPT; ++i) {
+                    const int p = 64 * i + lane;  // piece p of the image: row p / PPR, slot p % PPR
+                    const int r = p / PPR;
+                    dma16(rk, slot + M::kK + 1024 * i, r * row_b16 + 16 * ((p % PPR) ^ k_swz<D>(r)));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int p = 64 * i + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
+                    dma16(rv, slot + M::kV + 1024 * i, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
+                }
+            }
+        };
+        // chunk n's output block from sO to o: 16-byte pieces, lane -> row
+        // lane / 4 + 16 i, columns 4 (lane % 4) + 0..3 of the block
+        float* const obase = o + ((static_cast<size_t>(b) * T) * H + h) * D + cb * 16 + 4 * (lane & 3);
+        auto store_o = [&](int n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * i + (lane >> 2);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&sO[r][4 * (lane & 3)]);
+                const int tok = n * kC + r;
+                if (tok < T) *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * D) = x;
+            }
+        };
+        load(0);
+        vm_wait_all();
+        for (int n = 0; n < NC; ++n) {
+            lds_barrier();  // B1
+            if (n + 1 < NC) load(n + 1);  // slot (n + 1) & 1 was last read before this barrier
+            if (l == kLoadWaves - 1 && n > 0) store_o(n - 1);
+            lds_barrier();  // B2
+            lds_barrier();  // B3
+            vm_wait_all();  // the next chunk's slot is complete before its B1
+        }
+        lds_barrier();  // the output of the last chunk is in LDS
+        if (l == kLoadWaves - 1) store_o(NC - 1);
+        vm_wait_all();
+    }
 }
 
 template <int D>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    // An odd chunk count gets one more chunk past the sequence end: all its
-    // rows read zeros and beta = g = 0 there, so it leaves the state exactly
-    // unchanged (exp(0) S + K^T 0) and writes no output.  The chain then
-    // walks chunks in pairs with two operand buffers.
-    int NC = (a.T + kC - 1) / kC;
-    NC += NC & 1;
+    const int NC = (a.T + kC - 1) / kC;
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     char* ws = static_cast<char*>(a.workspace);
     hipLaunchKernelGGL(prefill_prep_kernel<D>, dim3(bh * NC), dim3(64), 0, stream,
@@ -584,9 +686,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                        a.beta, ws, a.T, a.H, NC);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, a.T, a.H, NC);
+    hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(kChainThreads), 0, stream,
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.state,
+                       a.o, ws, a.T, a.H, NC);
     return hipGetLastError();
 }
 
