@@ -20,15 +20,14 @@
 //        to the workspace as ready-made MFMA A operands (T1 and QKm as bf16
 //        hi + lo pairs, x = hi + lo to ~2^-17), in the order the chain
 //        kernel reads them, plus the gate factors.
-//  chain (one workgroup of two wavefronts per head and 16 state columns,
-//        serial over chunks):
-//        the state wavefront keeps the d_k x 16 fp32 state block in MFMA
-//        accumulators and per chunk forms X = K S, R = V - exp(G) X,
-//        W = T1 R and S <- exp(G_last) S + K^T (exp(G_last - G) W); each
-//        product's result feeds the next product from registers;
-//        the output wavefront runs one chunk behind and forms
-//        O = exp(G) Q S + QKm W from the chunk start state and W that the
-//        state wavefront leaves in LDS.  The two meet at one barrier per chunk.
+//  chain (one workgroup per head and 16 state columns, serial over chunks):
+//        four state wavefronts hold the d_k x 16 fp32 state block in MFMA
+//        accumulators and per chunk form X = K S, R = V - exp(G) X, W = T1 R
+//        and S <- exp(G_last) S + K^T (exp(G_last - G) W), exchanging R, W
+//        and the bf16 state through LDS (three barriers per chunk); four
+//        output wavefronts form O = exp(G) Q S + QKm W alongside;
+//        loader wavefronts fill a three-chunk LDS ring with direct-to-LDS
+//        loads two chunks ahead, and a storer wavefront writes O.
 //        Products whose rounding would reach the carried state or the output
 //        visibly use hi/lo operand pairs (T1 R, QKm W, K^T W').
 //
@@ -57,10 +56,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // Workspace: one block per (sequence, head, chunk), written by the prep
 // kernel in the order the chain kernel reads it, so that each chain load
 // instruction reads 1 KiB of contiguous memory:
-//   QF   Q as A operands, [row tile 4][k-step D/32][lane 64][8 bf16] (plain k order)
+//   QF   Q as A operands, [row tile 4][k-step D/32][lane 64][8 bf16] (split k order)
 //   T1F  T1 as A operands, [row tile 4][k-step 2][hi, lo][lane 64][8 bf16] (split k order)
 //   QKF  the decay-masked Q K^T as A operands, same shape and order as T1F
-//   E    exp(G_r) [64 fp32], exp(G_last - G_r) [64 fp32], exp(G_last), padding to 1 KiB
+//   E    fp32 [64] exp(G_r), [64] exp(G_last - G_r), [1] exp(G_last) at float 128;
+//        1 KiB in all
 template <int D>
 struct Ws {
     static constexpr int KS = D / 32;  // MFMA k-steps over d_k
@@ -71,6 +71,8 @@ struct Ws {
     static constexpr int kBlock = kE + 1024;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
+// float offsets inside E
+constexpr int kEg = 0, kEr = 64, kEl = 128;
 
 // Byte offset of A operand (row tile t, k-step ks, hi/lo hl) of lane `lane` in T1F / QKF.
 __host__ __device__ constexpr int frag_off(int t, int ks, int hl, int lane) {
@@ -152,10 +154,15 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait for all of this wavefront's outstanding global and direct-to-LDS
-// loads (s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained; the compiler
-// sees the wait and counts from it).
-__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Wait until at most N of this wavefront's global and direct-to-LDS loads
+// are outstanding (s_waitcnt vmcnt(N) in the gfx9 encoding, expcnt and
+// lgkmcnt unconstrained; the compiler sees the wait and counts from it).
+template <int N>
+__device__ __forceinline__ void vm_wait_keep() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+__device__ __forceinline__ void vm_wait_all() { vm_wait_keep<0>(); }
 
 // Transposing LDS read (ds_read_tr16_b64): within each 16-lane group, lane
 // i receives element i%4 of the 8-byte words that lanes 4j + i/4 point at,
@@ -224,9 +231,9 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     {
         float* e = reinterpret_cast<float*>(wsb + L::kE);
         const float Glast = __shfl(G, 63, 64);
-        e[lane] = expf(G);
-        e[64 + lane] = expf(Glast - G);
-        if (lane == 0) e[128] = expf(Glast);
+        e[kEg + lane] = expf(G);
+        e[kEr + lane] = expf(Glast - G);
+        if (lane == 0) e[kEl] = expf(Glast);
     }
 
     // fragments of the chunk's q and k rows (zero beyond the sequence end)
@@ -256,9 +263,30 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             for (int rr = 0; rr < 4; ++rr) {
                 const int row = 16 * mt + 4 * grp + rr;
                 float a = 0.f;
-                if (col < row) a = sBeta[row] * expf(sG[row] - sG[col]) * acc[rr];
+                if (col < row) a = sBeta[row] * __expf(sG[row] - sG[col]) * acc[rr];
                 sA[row][col] = a;
             }
+        }
+    }
+
+    // Q rows as the chain's A operands in split k order (qs), and in plain
+    // k order (qp) for Q K^T below
+    bf16x8 qp[4][KS];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + lr;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 f = {0u, 0u, 0u, 0u};
+            qp[t][ks] = zero_bf16x8();
+            if (r < nvalid) {
+                const uint16_t* qr = row_ptr(q, r) + 32 * ks;
+                qp[t][ks] = ld16_bf16(qr + 8 * grp);
+                const u32x2 a = *reinterpret_cast<const u32x2*>(qr + 4 * grp);
+                const u32x2 c = *reinterpret_cast<const u32x2*>(qr + 16 + 4 * grp);
+                f = u32x4{a[0], a[1], c[0], c[1]};
+            }
+            *reinterpret_cast<u32x4*>(wsb + L::kQF + ((t * KS + ks) * 64 + lane) * 16) = f;
         }
     }
 
@@ -267,18 +295,6 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // transposed (K Q^T), so lane l holds row r = 16 rt + l%16 and the four
     // columns s = 16 st + 4 (l/16) + 0..3: the tiles st = 2 ks and 2 ks + 1
     // give exactly the 8 values of k-step ks in split order.
-    bf16x8 qf[4][KS];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int r = 16 * t + lr;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[t][ks] = r < nvalid ? ld16_bf16(row_ptr(q, r) + 32 * ks + 8 * grp) : zero_bf16x8();
-            // a q fragment is already the chain's A operand
-            *reinterpret_cast<u32x4*>(wsb + L::kQF + ((t * KS + ks) * 64 + lane) * 16) =
-                __builtin_bit_cast(u32x4, qf[t][ks]);
-        }
-    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + lr;
@@ -294,12 +310,12 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 if (st <= rt) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < KS; ++kk) acc = mfma(kf[st][kk], qf[rt][kk], acc);
+                    for (int kk = 0; kk < KS; ++kk) acc = mfma(kf[st][kk], qp[rt][kk], acc);
                     // acc[j] = q_r . k_(s0 + j)
                     float x[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        x[j] = (s0 + j <= r) ? expf(sG[r] - sG[s0 + j]) * acc[j] : 0.f;
+                        x[j] = (s0 + j <= r) ? __expf(sG[r] - sG[s0 + j]) * acc[j] : 0.f;
                     split4(x[0], x[1], x[2], x[3], hi[half], lo[half]);
                 }
             }
@@ -395,23 +411,31 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
                                              0, 0, 0);
 }
 
-// LDS layout of the chain kernel.  Two slots hold the operands of two
-// consecutive chunks: the workspace block as it is (Q, T1, QKm, gates), the
-// K image and the workgroup's V block.  Loader wavefronts fill one slot while
-// the others compute on the other.
+// LDS layout of the chain kernel.  A ring of three slots holds the operands
+// that several wavefronts read, for three consecutive chunks: the gate block
+// as it is in the workspace, the K image and the workgroup's V block.
+// Loader wavefronts fill the slot of chunk n + 2 while the others compute on
+// chunk n.  Operands that one wavefront reads alone (its T1 or Q rows) go
+// straight from memory to its registers.
 template <int D>
 struct ChainLds {
-    static constexpr int kWs = 0;                          // workspace block (Ws<D> layout)
-    static constexpr int kK = Ws<D>::kBlock;               // K image (k_at layout)
+    static constexpr int kE = 0;                           // gate block (Ws<D>::kE layout)
+    static constexpr int kK = kE + 1024;                   // K image (k_at layout)
     static constexpr int kV = kK + kC * D * 2;             // V block, [64][16] bf16
     static constexpr int kSlot = kV + kC * 16 * 2;
-    static constexpr int kWsPieces = Ws<D>::kBlock / 1024; // 1 KiB loads per workspace block
+    static constexpr int kLoads = 1 + kC * D * 2 / 1024 + 2;  // 1 KiB loads per chunk
 };
 
 constexpr int kStateWaves = 4;   // chunk rows 16 w.., state rows (d_k / 4) w..
 constexpr int kOutWaves = 4;     // chunk rows 16 w.. of the output
-constexpr int kLoadWaves = 3;
-constexpr int kChainThreads = 64 * (kStateWaves + kOutWaves + kLoadWaves);
+constexpr int kLoadWaves = 2;
+constexpr int kChainThreads = 64 * (kStateWaves + kOutWaves + kLoadWaves + 1);  // + the storer
+constexpr int kRing = 3;
+
+// Two 8-byte LDS reads -> one split-order operand (k = c + 0..3 and c + 16 + 0..3).
+__device__ __forceinline__ bf16x8 ld_split(const uint16_t* p0, const uint16_t* p1) {
+    return join(*reinterpret_cast<const u32x2*>(p0), *reinterpret_cast<const u32x2*>(p1));
+}
 
 template <int D>
 __global__ void __launch_bounds__(kChainThreads)
@@ -430,7 +454,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
     constexpr int CLD = kC + 8;        // padded row of sR, sW, sWp (bf16)
     constexpr int OLD = 20;            // padded row of sO (fp32)
 
-    __shared__ __attribute__((aligned(16))) char sL[2][M::kSlot];
+    __shared__ __attribute__((aligned(16))) char sL[kRing][M::kSlot];
     __shared__ __attribute__((aligned(16))) uint16_t sS[16][SLD];       // chunk start state, [col][d_k]
     __shared__ __attribute__((aligned(16))) uint16_t sR[2][16][CLD];    // R hi/lo, [col][chunk row]
     __shared__ __attribute__((aligned(16))) uint16_t sW[2][16][CLD];    // W hi/lo
@@ -460,6 +484,8 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
     const int b = bh / H;
     const int h = bh - b * H;
     const int col = cb * 16 + lr;
+    const char* wsh = ws + static_cast<size_t>(bh) * NC * L::kBlock;
+    auto ws_rsrc = [&](int n) { return make_rsrc(wsh + static_cast<size_t>(n) * L::kBlock, L::kBlock); };
 
     if (wave < kStateWaves) {
         // ======================= state wavefronts ==========================
@@ -478,26 +504,42 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
                 *reinterpret_cast<u32x2*>(&sS[lr][SRW * w + 16 * mt + 4 * grp]) =
                     to_bf16x4(S[mt][0], S[mt][1], S[mt][2], S[mt][3]);
         };
+        // T1 rows 16 w.. of a chunk, hi/lo, split k order (read by this wavefront only)
+        bf16x8 t1[2][2];
+        auto load_t1 = [&](int n) {
+            const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    t1[ks][hl] = as_bf16x8(buf_ld16(rw, L::kT1F + frag_off(w, ks, hl, lane)));
+        };
+        load_t1(0);
         publish_state();
 
         for (int n = 0; n < NC; ++n) {
-            const char* slot = sL[n & 1];
+            const char* slot = sL[n % kRing];
             const uint16_t* sK = reinterpret_cast<const uint16_t*>(slot + M::kK);
             const uint16_t* sV = reinterpret_cast<const uint16_t*>(slot + M::kV);
-            const float* E = reinterpret_cast<const float*>(slot + L::kE);
+            const float* E = reinterpret_cast<const float*>(slot + M::kE);
             lds_barrier();  // B1: chunk n's operands and start state are in LDS
 
-            // X = K S for chunk rows 16 w + l%16 (plain k order over d_k)
+            // X = K S for chunk rows 16 w + l%16 (split k order over d_k)
             f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = ld16_bf16(&sK[k_at<D>(16 * w + lr, 32 * ks + 8 * grp)]);
-                X = mfma(a, ld16_bf16(&sS[lr][32 * ks + 8 * grp]), X);
+                const int c = 32 * ks + 4 * grp;
+                const int r = 16 * w + lr;
+                X = mfma(ld_split(&sK[k_at<D>(r, c)], &sK[k_at<D>(r, c + 16)]),
+                         ld_split(&sS[lr][c], &sS[lr][c + 16]), X);
             }
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
+            const f32x4 er = *reinterpret_cast<const f32x4*>(&E[kEr + 16 * w + 4 * grp]);
+            const float el = E[kEl];
+            const u32x2 vv = ld_tr(&sV[(16 * w + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3)]);
+
             // R = V - exp(G) X for this wavefront's rows, hi/lo to LDS
             {
-                const u32x2 vv = ld_tr(&sV[(16 * w + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3)]);
-                const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[16 * w + 4 * grp]);
                 u32x2 rh, rl;
                 split4(__uint_as_float(vv[0] << 16) - eg[0] * X[0],
                        __uint_as_float(vv[0] & 0xffff0000u) - eg[1] * X[1],
@@ -513,18 +555,25 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int c = 32 * ks + 4 * grp;
-                const bf16x8 th = ld16_bf16(slot + L::kT1F + frag_off(w, ks, 0, lane));
-                const bf16x8 tl = ld16_bf16(slot + L::kT1F + frag_off(w, ks, 1, lane));
-                const bf16x8 rh = join(*reinterpret_cast<const u32x2*>(&sR[0][lr][c]),
-                                       *reinterpret_cast<const u32x2*>(&sR[0][lr][c + 16]));
-                const bf16x8 rl = join(*reinterpret_cast<const u32x2*>(&sR[1][lr][c]),
-                                       *reinterpret_cast<const u32x2*>(&sR[1][lr][c + 16]));
-                W = mfma(th, rh, W);
-                W = mfma(th, rl, W);
-                W = mfma(tl, rh, W);
+                const bf16x8 rh = ld_split(&sR[0][lr][c], &sR[0][lr][c + 16]);
+                const bf16x8 rl = ld_split(&sR[1][lr][c], &sR[1][lr][c + 16]);
+                W = mfma(t1[ks][0], rh, W);
+                W = mfma(t1[ks][0], rl, W);
+                W = mfma(t1[ks][1], rh, W);
             }
+            load_t1(min(n + 1, NC - 1));  // t1 is not read again in this chunk
+            // K^T operands of the state update (d_k rows SRW w + 16 mt + l%16,
+            // chunk rows in split order), read while W forms
+            bf16x8 kt[SMT][2];
+#pragma unroll
+            for (int mt = 0; mt < SMT; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int r = 32 * ks + 4 * grp + (lr >> 2);
+                    const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
+                    kt[mt][ks] = join(ld_tr(&sK[k_at<D>(r, cc)]), ld_tr(&sK[k_at<D>(r + 16, cc)]));
+                }
             {
-                const f32x4 er = *reinterpret_cast<const f32x4*>(&E[64 + 16 * w + 4 * grp]);
                 u32x2 wh, wl, ph, pl;
                 split4(W, wh, wl);
                 split4(er[0] * W[0], er[1] * W[1], er[2] * W[2], er[3] * W[3], ph, pl);
@@ -535,33 +584,26 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
             }
             lds_barrier();  // B3: all of W and W' are in LDS
 
-            // S <- exp(G_last) S + K^T W' for this wavefront's state rows.
-            // The K^T operand (d_k rows SRW w + 16 mt + l%16, chunk rows in
-            // split order) comes from two transposing reads of the K image.
-            const float el = E[128];
+            // S <- exp(G_last) S + K^T W' for this wavefront's state rows
+#pragma unroll
+            for (int mt = 0; mt < SMT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= el;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int c = 32 * ks + 4 * grp;
-                const bf16x8 ph = join(*reinterpret_cast<const u32x2*>(&sWp[0][lr][c]),
-                                       *reinterpret_cast<const u32x2*>(&sWp[0][lr][c + 16]));
-                const bf16x8 pl = join(*reinterpret_cast<const u32x2*>(&sWp[1][lr][c]),
-                                       *reinterpret_cast<const u32x2*>(&sWp[1][lr][c + 16]));
+                const bf16x8 ph = ld_split(&sWp[0][lr][c], &sWp[0][lr][c + 16]);
+                const bf16x8 pl = ld_split(&sWp[1][lr][c], &sWp[1][lr][c + 16]);
 #pragma unroll
                 for (int mt = 0; mt < SMT; ++mt) {
-                    if (ks == 0)
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= el;
-                    const int r = 32 * ks + 4 * grp + (lr >> 2);
-                    const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
-                    const bf16x8 a = join(ld_tr(&sK[k_at<D>(r, cc)]), ld_tr(&sK[k_at<D>(r + 16, cc)]));
-                    S[mt] = mfma(a, ph, S[mt]);
-                    S[mt] = mfma(a, pl, S[mt]);
+                    S[mt] = mfma(kt[mt][ks], ph, S[mt]);
+                    S[mt] = mfma(kt[mt][ks], pl, S[mt]);
                 }
             }
             // sS was last read before B2 (by every wavefront)
             publish_state();
         }
-        lds_barrier();  // the output of the last chunk is in LDS
+        lds_barrier();  // final barrier, matched by every wavefront
 
 #pragma unroll
         for (int mt = 0; mt < SMT; ++mt)
@@ -573,106 +615,144 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
     if (wave < kStateWaves + kOutWaves) {
         // ====================== output wavefronts ==========================
         const int w = wave - kStateWaves;
-        for (int n = 0; n < NC; ++n) {
-            const char* slot = sL[n & 1];
-            const float* E = reinterpret_cast<const float*>(slot + L::kE);
-            lds_barrier();  // B1
-            // P = Q S for chunk rows 16 w + l%16
-            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+        // Q rows 16 w + l%16 and QKm rows 16 w.. hi/lo, split k order (read
+        // by this wavefront only)
+        bf16x8 qf[KS];
+        bf16x8 qk[2][2];
+        auto load_q = [&](int n) {
+            const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                O = mfma(ld16_bf16(slot + L::kQF + ((w * KS + ks) * 64 + lane) * 16),
-                         ld16_bf16(&sS[lr][32 * ks + 8 * grp]), O);
+                qf[ks] = as_bf16x8(buf_ld16(rw, L::kQF + ((w * KS + ks) * 64 + lane) * 16));
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    qk[ks][hl] = as_bf16x8(buf_ld16(rw, L::kQKF + frag_off(w, ks, hl, lane)));
+        };
+        load_q(0);
+        for (int n = 0; n < NC; ++n) {
+            const float* E = reinterpret_cast<const float*>(sL[n % kRing] + M::kE);
+            lds_barrier();  // B1
+            // P = Q S
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = 32 * ks + 4 * grp;
+                P = mfma(qf[ks], ld_split(&sS[lr][c], &sS[lr][c + 16]), P);
+            }
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
             lds_barrier();  // B2
             lds_barrier();  // B3: W is in LDS
             // O = exp(G) P + QKm W
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[16 * w + 4 * grp]);
+            f32x4 O;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) O[rr] *= eg[rr];
+            for (int rr = 0; rr < 4; ++rr) O[rr] = eg[rr] * P[rr];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks > w) continue;  // QKm is zero there
                 const int c = 32 * ks + 4 * grp;
-                const bf16x8 wh = join(*reinterpret_cast<const u32x2*>(&sW[0][lr][c]),
-                                       *reinterpret_cast<const u32x2*>(&sW[0][lr][c + 16]));
-                const bf16x8 wl = join(*reinterpret_cast<const u32x2*>(&sW[1][lr][c]),
-                                       *reinterpret_cast<const u32x2*>(&sW[1][lr][c + 16]));
-                const bf16x8 qh = ld16_bf16(slot + L::kQKF + frag_off(w, ks, 0, lane));
-                const bf16x8 ql = ld16_bf16(slot + L::kQKF + frag_off(w, ks, 1, lane));
-                O = mfma(qh, wh, O);
-                O = mfma(qh, wl, O);
-                O = mfma(ql, wh, O);
+                const bf16x8 wh = ld_split(&sW[0][lr][c], &sW[0][lr][c + 16]);
+                const bf16x8 wl = ld_split(&sW[1][lr][c], &sW[1][lr][c + 16]);
+                O = mfma(qk[ks][0], wh, O);
+                O = mfma(qk[ks][0], wl, O);
+                O = mfma(qk[ks][1], wh, O);
             }
-            // to LDS; a loader wavefront stores the block during the next
-            // chunk (the last loader read sO before this chunk's B2)
+            load_q(min(n + 1, NC - 1));  // qf and qk are not read again in this chunk
+            // to LDS; the storer writes the block during the next chunk
+            // (it read the previous block before this chunk's B2)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sO[16 * w + 4 * grp + rr][lr] = O[rr];
         }
-        lds_barrier();  // the output of the last chunk is in LDS
+        lds_barrier();  // final barrier: the last chunk's output is in LDS
         return;
     }
-    {
+    if (wave < kStateWaves + kOutWaves + kLoadWaves) {
         // ====================== loader wavefronts ==========================
-        // Each fills its share of the next chunk's slot with direct-to-LDS
-        // loads and waits for them before the next chunk's first barrier, so
-        // the other wavefronts read the slot after that barrier.
+        // Each loader issues the same number of 1 KiB direct-to-LDS loads per
+        // chunk (kPer, the last one repeated where the count does not
+        // divide), in three parts, one after each barrier.  The loads of
+        // chunk n + 2 go out during chunk n, and before chunk n + 1's first
+        // barrier each loader waits until only its kPer newest loads (those
+        // of chunk n + 2) may be outstanding.
         const int l = wave - kStateWaves - kOutWaves;
         const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;  // element of (b, t=0, h, 0)
         const int row_b16 = H * D * 2;                                  // bytes per token, bf16
         const int seq_b16 = (T - 1) * row_b16 + D * 2;  // end of the last valid row
-        const char* wsh = ws + static_cast<size_t>(bh) * NC * L::kBlock;
-        // workspace pieces [lo, hi) for this loader; the last one also loads K and V
-        constexpr int kShare = (M::kWsPieces + KPT + 2 + kLoadWaves - 1) / kLoadWaves;
-        const int lo = min(l * kShare, M::kWsPieces);
-        const int hi = (l == kLoadWaves - 1) ? M::kWsPieces : min(lo + kShare, M::kWsPieces);
-        auto load = [&](int n) {
-            char* slot = sL[n & 1];
-            const __amdgpu_buffer_rsrc_t rw =
-                make_rsrc(wsh + static_cast<size_t>(n) * L::kBlock, L::kBlock);
-            for (int i = lo; i < hi; ++i) dma16(rw, slot + M::kWs + 1024 * i, 1024 * i + 16 * lane);
-            if (l == kLoadWaves - 1) {
-                const int r0 = n * kC;
-                const __amdgpu_buffer_rsrc_t rk =
-                    make_rsrc(k + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
-                const __amdgpu_buffer_rsrc_t rv =
-                    make_rsrc(v + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+        constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
+        constexpr int kPart = (kPer + 2) / 3;
+        auto load = [&](int n, int q) {
+            char* slot = sL[n % kRing];
+            const int r0 = n * kC;
+            const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
+            const __amdgpu_buffer_rsrc_t rk =
+                make_rsrc(k + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+            const __amdgpu_buffer_rsrc_t rv =
+                make_rsrc(v + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
 #pragma unroll
-                for (int i = 0; i < KPT; ++i) {
-                    const int p = 64 * i + lane;  // piece p of the image: row p / PPR, slot p % PPR
-                    const int r = p / PPR;
-                    dma16(rk, slot + M::kK + 1024 * i, r * row_b16 + 16 * ((p % PPR) ^ k_swz<D>(r)));
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int p = 64 * i + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
-                    dma16(rv, slot + M::kV + 1024 * i, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
+            for (int jj = 0; jj < kPart; ++jj) {
+                const int j = kPart * q + jj;
+                if (j >= kPer) break;
+                const int i = min(kPer * l + j, M::kLoads - 1);
+                if (i == 0) {
+                    dma16(rw, slot + M::kE, L::kE + 16 * lane);
+                } else if (i < 1 + KPT) {
+                    const int p = 64 * (i - 1) + lane;  // image piece: row p / PPR, slot p % PPR
+                    const int rr = p / PPR;
+                    dma16(rk, slot + M::kK + 1024 * (i - 1), rr * row_b16 + 16 * ((p % PPR) ^ k_swz<D>(rr)));
+                } else {
+                    const int jv = i - 1 - KPT;
+                    const int p = 64 * jv + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
+                    dma16(rv, slot + M::kV + 1024 * jv, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
                 }
             }
         };
-        // chunk n's output block from sO to o: 16-byte pieces, lane -> row
-        // lane / 4 + 16 i, columns 4 (lane % 4) + 0..3 of the block
+        for (int q = 0; q < 3; ++q) load(0, q);
+        if (NC > 1)
+            for (int q = 0; q < 3; ++q) load(1, q);
+        vm_wait_all();
+        for (int n = 0; n < NC; ++n) {
+            const bool more = n + 2 < NC;  // slot (n + 2) % 3 was last read before B1
+            lds_barrier();  // B1
+            if (more) load(n + 2, 0);
+            lds_barrier();  // B2
+            if (more) load(n + 2, 1);
+            lds_barrier();  // B3
+            if (more) {
+                load(n + 2, 2);
+                vm_wait_keep<kPer>();  // chunk n + 1's loads are done
+            } else {
+                vm_wait_all();
+            }
+        }
+        lds_barrier();  // final barrier
+        return;
+    }
+    {
+        // ======================= storer wavefront ==========================
+        // chunk n's output block from sO to o: lane -> row lane / 4 + 16 i,
+        // columns 4 (lane % 4) + 0..3 of the block, read as two 8-byte halves
         float* const obase = o + ((static_cast<size_t>(b) * T) * H + h) * D + cb * 16 + 4 * (lane & 3);
         auto store_o = [&](int n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * i + (lane >> 2);
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&sO[r][4 * (lane & 3)]);
-                const int tok = n * kC + r;
-                if (tok < T) *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * D) = x;
+                const int rr = 16 * i + (lane >> 2);
+                const float* src = &sO[rr][4 * (lane & 3)];
+                const f32x2 a = *reinterpret_cast<const f32x2*>(src);
+                const f32x2 c = *reinterpret_cast<const f32x2*>(src + 2);
+                const int tok = n * kC + rr;
+                if (tok < T)
+                    *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * D) = f32x4{a[0], a[1], c[0], c[1]};
             }
         };
-        load(0);
-        vm_wait_all();
         for (int n = 0; n < NC; ++n) {
-            lds_barrier();  // B1
-            if (n + 1 < NC) load(n + 1);  // slot (n + 1) & 1 was last read before this barrier
-            if (l == kLoadWaves - 1 && n > 0) store_o(n - 1);
+            lds_barrier();  // B1: chunk n - 1's output is in sO
+            if (n > 0) store_o(n - 1);
             lds_barrier();  // B2
             lds_barrier();  // B3
-            vm_wait_all();  // the next chunk's slot is complete before its B1
         }
-        lds_barrier();  // the output of the last chunk is in LDS
-        if (l == kLoadWaves - 1) store_o(NC - 1);
-        vm_wait_all();
+        lds_barrier();  // final barrier
+        store_o(NC - 1);
     }
 }
 
