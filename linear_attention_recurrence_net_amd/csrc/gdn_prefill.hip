@@ -16,10 +16,10 @@
 // Two kernels:
 //  prep  (one wavefront per chunk and head, all chunks in parallel): G,
 //        K K^T and Q K^T on MFMA, the gate masks, the unit lower triangular
-//        inverse T by forward substitution in fp32.  It writes Q, T1 and QKm
-//        to the workspace as ready-made MFMA A operands (T1 and QKm as bf16
-//        hi + lo pairs, x = hi + lo to ~2^-17), in the order the chain
-//        kernel reads them, plus the gate factors.
+//        inverse T by forward substitution in fp32.  It writes T1 and QKm to
+//        the workspace as ready-made MFMA A operands (bf16 hi + lo pairs,
+//        x = hi + lo to ~2^-17), in the order the chain kernel reads them,
+//        plus the gate factors.
 //  chain (one workgroup per head and 16 state columns, serial over chunks):
 //        four state wavefronts hold the d_k x 16 fp32 state block in MFMA
 //        accumulators and per chunk form X = K S, R = V - exp(G) X, W = T1 R
@@ -56,7 +56,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // Workspace: one block per (sequence, head, chunk), written by the prep
 // kernel in the order the chain kernel reads it, so that each chain load
 // instruction reads 1 KiB of contiguous memory:
-//   QF   Q as A operands, [row tile 4][k-step D/32][lane 64][8 bf16] (split k order)
 //   T1F  T1 as A operands, [row tile 4][k-step 2][hi, lo][lane 64][8 bf16] (split k order)
 //   QKF  the decay-masked Q K^T as A operands, same shape and order as T1F
 //   E    fp32 [64] exp(G_r), [64] exp(G_last - G_r), [1] exp(G_last) at float 128;
@@ -64,8 +63,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 template <int D>
 struct Ws {
     static constexpr int KS = D / 32;  // MFMA k-steps over d_k
-    static constexpr int kQF = 0;
-    static constexpr int kT1F = kQF + 4 * KS * 64 * 16;
+    static constexpr int kT1F = 0;
     static constexpr int kQKF = kT1F + 4 * 2 * 2 * 64 * 16;
     static constexpr int kE = kQKF + 4 * 2 * 2 * 64 * 16;
     static constexpr int kBlock = kE + 1024;
@@ -269,25 +267,14 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
     }
 
-    // Q rows as the chain's A operands in split k order (qs), and in plain
-    // k order (qp) for Q K^T below
+    // fragments of the chunk's q rows (zero beyond the sequence end)
     bf16x8 qp[4][KS];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + lr;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 f = {0u, 0u, 0u, 0u};
-            qp[t][ks] = zero_bf16x8();
-            if (r < nvalid) {
-                const uint16_t* qr = row_ptr(q, r) + 32 * ks;
-                qp[t][ks] = ld16_bf16(qr + 8 * grp);
-                const u32x2 a = *reinterpret_cast<const u32x2*>(qr + 4 * grp);
-                const u32x2 c = *reinterpret_cast<const u32x2*>(qr + 16 + 4 * grp);
-                f = u32x4{a[0], a[1], c[0], c[1]};
-            }
-            *reinterpret_cast<u32x4*>(wsb + L::kQF + ((t * KS + ks) * 64 + lane) * 16) = f;
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            qp[t][ks] = r < nvalid ? ld16_bf16(row_ptr(q, r) + 32 * ks + 8 * grp) : zero_bf16x8();
     }
 
     // QKm = lower part (diagonal included) of exp(G_r - G_s) o (Q K^T), as
@@ -411,19 +398,21 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
                                              0, 0, 0);
 }
 
-// LDS layout of the chain kernel.  A ring of three slots holds the operands
-// that several wavefronts read, for three consecutive chunks: the gate block
-// as it is in the workspace, the K image and the workgroup's V block.
-// Loader wavefronts fill the slot of chunk n + 2 while the others compute on
-// chunk n.  Operands that one wavefront reads alone (its T1 or Q rows) go
+// LDS layout of the chain kernel.  A ring of three slots holds, for three
+// consecutive chunks, the operands that arrive as whole rows: the gate block
+// as it is in the workspace, the K and Q images (k_at layout) and the
+// workgroup's V block.  Loader wavefronts fill the slot of chunk n + 2 while
+// the others compute on chunk n.  Operands that one wavefront reads alone
+// and that the workspace holds in fragment order (its T1 or QKm rows) go
 // straight from memory to its registers.
 template <int D>
 struct ChainLds {
     static constexpr int kE = 0;                           // gate block (Ws<D>::kE layout)
-    static constexpr int kK = kE + 1024;                   // K image (k_at layout)
-    static constexpr int kV = kK + kC * D * 2;             // V block, [64][16] bf16
+    static constexpr int kK = kE + 1024;                   // K image
+    static constexpr int kQ = kK + kC * D * 2;             // Q image
+    static constexpr int kV = kQ + kC * D * 2;             // V block, [64][16] bf16
     static constexpr int kSlot = kV + kC * 16 * 2;
-    static constexpr int kLoads = 1 + kC * D * 2 / 1024 + 2;  // 1 KiB loads per chunk
+    static constexpr int kLoads = 1 + 2 * (kC * D * 2 / 1024) + 2;  // 1 KiB loads per chunk
 };
 
 constexpr int kStateWaves = 4;   // chunk rows 16 w.., state rows (d_k / 4) w..
@@ -439,9 +428,9 @@ __device__ __forceinline__ bf16x8 ld_split(const uint16_t* p0, const uint16_t* p
 
 template <int D>
 __global__ void __launch_bounds__(kChainThreads)
-prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                     float* __restrict__ state, float* __restrict__ o,
-                     const char* __restrict__ ws, int T, int H, int NC) {
+prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, float* __restrict__ state,
+                     float* __restrict__ o, const char* __restrict__ ws, int T, int H, int NC) {
     using L = Ws<D>;
     using M = ChainLds<D>;
     constexpr int NCB = D / 16;        // column blocks per head
@@ -615,15 +604,10 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
     if (wave < kStateWaves + kOutWaves) {
         // ====================== output wavefronts ==========================
         const int w = wave - kStateWaves;
-        // Q rows 16 w + l%16 and QKm rows 16 w.. hi/lo, split k order (read
-        // by this wavefront only)
-        bf16x8 qf[KS];
+        // QKm rows 16 w.. hi/lo, split k order (read by this wavefront only)
         bf16x8 qk[2][2];
         auto load_q = [&](int n) {
             const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[ks] = as_bf16x8(buf_ld16(rw, L::kQF + ((w * KS + ks) * 64 + lane) * 16));
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -632,14 +616,18 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
         };
         load_q(0);
         for (int n = 0; n < NC; ++n) {
-            const float* E = reinterpret_cast<const float*>(sL[n % kRing] + M::kE);
+            const char* slot = sL[n % kRing];
+            const uint16_t* sQ = reinterpret_cast<const uint16_t*>(slot + M::kQ);
+            const float* E = reinterpret_cast<const float*>(slot + M::kE);
             lds_barrier();  // B1
-            // P = Q S
+            // P = Q S for chunk rows 16 w + l%16 (split k order over d_k)
             f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int c = 32 * ks + 4 * grp;
-                P = mfma(qf[ks], ld_split(&sS[lr][c], &sS[lr][c + 16]), P);
+                const int rq = 16 * w + lr;
+                P = mfma(ld_split(&sQ[k_at<D>(rq, c)], &sQ[k_at<D>(rq, c + 16)]),
+                         ld_split(&sS[lr][c], &sS[lr][c + 16]), P);
             }
             const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
             lds_barrier();  // B2
@@ -658,7 +646,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
                 O = mfma(qk[ks][0], wl, O);
                 O = mfma(qk[ks][1], wh, O);
             }
-            load_q(min(n + 1, NC - 1));  // qf and qk are not read again in this chunk
+            load_q(min(n + 1, NC - 1));  // qk is not read again in this chunk
             // to LDS; the storer writes the block during the next chunk
             // (it read the previous block before this chunk's B2)
 #pragma unroll
@@ -681,35 +669,40 @@ prefill_chain_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict_
         const int seq_b16 = (T - 1) * row_b16 + D * 2;  // end of the last valid row
         constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
         constexpr int kPart = (kPer + 2) / 3;
-        auto load = [&](int n, int q) {
+        auto load = [&](int n, int qt) {
             char* slot = sL[n % kRing];
             const int r0 = n * kC;
             const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
             const __amdgpu_buffer_rsrc_t rk =
                 make_rsrc(k + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+            const __amdgpu_buffer_rsrc_t rq =
+                make_rsrc(q + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
             const __amdgpu_buffer_rsrc_t rv =
                 make_rsrc(v + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
 #pragma unroll
             for (int jj = 0; jj < kPart; ++jj) {
-                const int j = kPart * q + jj;
+                const int j = kPart * qt + jj;
                 if (j >= kPer) break;
                 const int i = min(kPer * l + j, M::kLoads - 1);
                 if (i == 0) {
                     dma16(rw, slot + M::kE, L::kE + 16 * lane);
-                } else if (i < 1 + KPT) {
-                    const int p = 64 * (i - 1) + lane;  // image piece: row p / PPR, slot p % PPR
+                } else if (i < 1 + 2 * KPT) {
+                    const bool isq = i >= 1 + KPT;  // K image pieces, then Q image pieces
+                    const int pi = i - 1 - (isq ? KPT : 0);
+                    const int p = 64 * pi + lane;  // image piece: row p / PPR, slot p % PPR
                     const int rr = p / PPR;
-                    dma16(rk, slot + M::kK + 1024 * (i - 1), rr * row_b16 + 16 * ((p % PPR) ^ k_swz<D>(rr)));
+                    dma16(isq ? rq : rk, slot + (isq ? M::kQ : M::kK) + 1024 * pi,
+                          rr * row_b16 + 16 * ((p % PPR) ^ k_swz<D>(rr)));
                 } else {
-                    const int jv = i - 1 - KPT;
+                    const int jv = i - 1 - 2 * KPT;
                     const int p = 64 * jv + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
                     dma16(rv, slot + M::kV + 1024 * jv, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
                 }
             }
         };
-        for (int q = 0; q < 3; ++q) load(0, q);
+        for (int qt = 0; qt < 3; ++qt) load(0, qt);
         if (NC > 1)
-            for (int q = 0; q < 3; ++q) load(1, q);
+            for (int qt = 0; qt < 3; ++qt) load(1, qt);
         vm_wait_all();
         for (int n = 0; n < NC; ++n) {
             const bool more = n + 2 < NC;  // slot (n + 2) % 3 was last read before B1
@@ -767,8 +760,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(kChainThreads), 0, stream,
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.state,
-                       a.o, ws, a.T, a.H, NC);
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, a.T, a.H, NC);
     return hipGetLastError();
 }
 
