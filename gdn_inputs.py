@@ -21,6 +21,7 @@ float64 upcasts of them, so input rounding is not a source of disagreement.
 
 Layouts (row-major, last axis contiguous):
   q, k  [B, T, H, d_k]      v, o  [B, T, H, d_v]
+        (q, k [B, T, H_qk, d_k] for a case whose value heads share H_qk q/k heads)
   g     [B, T, H]  (GDA: one log-gate per head and token)
         [B, T, H, d_k]  (KDA: one log-gate per key row)
   beta  [B, T, H]
@@ -77,7 +78,7 @@ class Case:
 
     B: int
     T: int
-    H: int
+    H: int  # value heads (v, g, beta, state, o)
     d_k: int
     d_v: int
     K: int
@@ -90,6 +91,11 @@ class Case:
     beta: np.ndarray
     state: np.ndarray  # [B,H,K,d_k,d_v] float32, slot 0 = S0, other slots 0
     accepted: np.ndarray | None  # [B] int32
+
+    @property
+    def H_qk(self) -> int:
+        """Heads of q and k (H unless the value heads share q/k heads)."""
+        return self.q.shape[2]
 
     def qkv_bits(self, name: str) -> np.ndarray:
         assert self.qkv_dtype == "bf16"
@@ -122,10 +128,18 @@ def make_case(
     zero_state: bool = False,
     with_accepted: bool = False,
     q_scale: bool = True,
+    H_qk: int | None = None,
 ) -> Case:
-    """Draw one seeded case (see the module docstring for the recipe)."""
+    """Draw one seeded case (see the module docstring for the recipe).
+
+    H_qk: number of q/k heads (default H); the value heads then share them.
+    """
     if d_v is None:
         d_v = d_k
+    if H_qk is None:
+        H_qk = H
+    if H_qk < 1 or H % H_qk != 0:
+        raise ValueError(f"H_qk={H_qk} must divide H={H}")
     if gate not in ("gda", "kda"):
         raise ValueError(gate)
     if qkv_dtype not in ("bf16", "f32"):
@@ -134,10 +148,10 @@ def make_case(
     s0 = rng.normal(0.0, 0.1, size=(B, H, d_k, d_v))
     if zero_state:
         s0 = np.zeros_like(s0)
-    q = _l2n(rng.standard_normal((B, T, H, d_k)))
+    q = _l2n(rng.standard_normal((B, T, H_qk, d_k)))
     if q_scale:
         q = q * (1.0 / math.sqrt(d_k))
-    k = _l2n(rng.standard_normal((B, T, H, d_k)))
+    k = _l2n(rng.standard_normal((B, T, H_qk, d_k)))
     v = rng.standard_normal((B, T, H, d_v))
     beta_raw = rng.standard_normal((B, T, H))
     gshape = (B, T, H) if gate == "gda" else (B, T, H, d_k)

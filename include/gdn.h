@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,        /* a required pointer is NULL                      */
-    GDN_ERR_SHAPE = 2,       /* a size is negative, or K < 1, or chunk < 1      */
+    GDN_ERR_SHAPE = 2,       /* a size is negative, K < 1, chunk < 1, or H_qk
+                                does not divide H                               */
     GDN_ERR_UNSUPPORTED = 3, /* d_k != d_v, d not in {64,128}, bad dtype/gate   */
     GDN_ERR_WORKSPACE = 4,   /* prefill workspace missing or too small          */
     GDN_ERR_HIP = 5          /* the HIP runtime reported a launch error         */
@@ -120,6 +121,46 @@ int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_
                         int32_t chunk, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, float* state, float* o,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * q/k shared between value heads, without materialising the repeats
+ * (llama.cpp commit log, tag b9752, bullet "models : avoid Q and K repeats
+ * when using fused GDA").  H value heads (v, g, beta, state, o) read H_qk
+ * query/key heads, H a multiple of H_qk, in one of two orders (the same
+ * page's bullet "reorder v heads for linear attention to avoid expensive
+ * interleaved repeat" names both: the interleaved repeat, and the value-head
+ * order that replaces it):
+ */
+typedef enum {
+    GDN_HEADS_GROUPED = 0, /* value head h reads q/k head h / (H / H_qk)      */
+    GDN_HEADS_TILED = 1    /* value head h reads q/k head h % H_qk            */
+} gdn_head_map;
+
+/*
+ * gdn_forward_snapshots with shared q/k heads: q, k [B,T,H_qk,d_k]; every
+ * other argument as in gdn_forward_snapshots (K = 1 is the in-place
+ * single-slot forward).  The results are bit-identical to
+ * gdn_forward_snapshots on q and k repeated to H heads in the given order.
+ * H_qk < 1 or H not a multiple of H_qk (with H > 0) -> GDN_ERR_SHAPE;
+ * head_map not a gdn_head_map -> GDN_ERR_UNSUPPORTED.
+ */
+int gdn_forward_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                             int32_t d_k, int32_t d_v, int32_t qkv_dtype, int32_t gate,
+                             int32_t K, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state,
+                             float* final_state, float* o, void* stream);
+
+/*
+ * gdn_prefill_chunked with shared q/k heads: q, k [B,T,H_qk,d_k]; every
+ * other argument, the workspace size (gdn_prefill_workspace_size with the H
+ * value heads) and the errors as above.  The results are bit-identical to
+ * gdn_prefill_chunked on q and k repeated to H heads in the given order.
+ */
+int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                     int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                     const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, float* state, float* o,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gdn_status_str(int status);

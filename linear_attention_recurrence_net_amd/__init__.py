@@ -8,14 +8,17 @@ library is missing or a tensor is not on the GPU, the call raises.
 
 Entry points (same names as the C ABI):
   gdn_forward, gdn_forward_snapshots, gdn_rollback_select,
-  gdn_prefill_workspace_size, gdn_prefill_chunked
+  gdn_prefill_workspace_size, gdn_prefill_chunked,
+  gdn_forward_qk_broadcast, gdn_prefill_chunked_qk_broadcast
 """
 
 from ._binding import (  # noqa: F401
     GdnError,
     gdn_forward,
+    gdn_forward_qk_broadcast,
     gdn_forward_snapshots,
     gdn_prefill_chunked,
+    gdn_prefill_chunked_qk_broadcast,
     gdn_prefill_workspace_size,
     gdn_rollback_select,
     library,

@@ -12,6 +12,9 @@ _LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
+GDN_HEADS_GROUPED, GDN_HEADS_TILED = 0, 1
+_HEAD_MAPS = {"grouped": GDN_HEADS_GROUPED, "tiled": GDN_HEADS_TILED,
+              GDN_HEADS_GROUPED: GDN_HEADS_GROUPED, GDN_HEADS_TILED: GDN_HEADS_TILED}
 
 EXPORTED = (
     "gdn_forward",
@@ -19,6 +22,8 @@ EXPORTED = (
     "gdn_rollback_select",
     "gdn_prefill_workspace_size",
     "gdn_prefill_chunked",
+    "gdn_forward_qk_broadcast",
+    "gdn_prefill_chunked_qk_broadcast",
     "gdn_status_str",
 )
 
@@ -58,6 +63,10 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_workspace_size.restype = sz
     lib.gdn_prefill_chunked.argtypes = [i32] * 6 + [vp] * 8 + [sz, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_forward_qk_broadcast.argtypes = [i32] * 10 + [vp] * 9
+    lib.gdn_forward_qk_broadcast.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_qk_broadcast.argtypes = [i32] * 8 + [vp] * 8 + [sz, vp]
+    lib.gdn_prefill_chunked_qk_broadcast.restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -95,17 +104,23 @@ def _shape(name: str, t: torch.Tensor, shape) -> None:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _qkv_gate(q, k, v, g, beta):
+def _qkv_gate(q, k, v, g, beta, shared_qk=False):
+    """Check q, k, v, g, beta; with shared_qk, q and k may have H_qk heads
+    (a divisor of v's H).  Returns B, T, H, dk, dv, dtype, gate, device (and
+    H_qk with shared_qk)."""
     _dev_tensor("q", q, (torch.float32, torch.bfloat16))
     dev = q.device
     if q.dim() != 4:
-        raise ValueError("q must be [B,T,H,d_k]")
-    B, T, H, dk = q.shape
+        raise ValueError("q must be [B,T,H_qk,d_k]" if shared_qk else "q must be [B,T,H,d_k]")
+    B, T, Hq, dk = q.shape
     _dev_tensor("k", k, (q.dtype,), dev)
     _dev_tensor("v", v, (q.dtype,), dev)
-    _shape("k", k, (B, T, H, dk))
-    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+    _shape("k", k, (B, T, Hq, dk))
+    if v.dim() != 4 or tuple(v.shape[:2]) != (B, T) or (not shared_qk and v.shape[2] != Hq):
         raise ValueError("v must be [B,T,H,d_v]")
+    H = v.shape[2]
+    if shared_qk and (Hq < 1 or H % Hq != 0):
+        raise ValueError(f"v has {H} heads, not a multiple of the {Hq} q/k heads")
     dv = v.shape[3]
     _dev_tensor("g", g, (torch.float32,), dev)
     _dev_tensor("beta", beta, (torch.float32,), dev)
@@ -117,6 +132,8 @@ def _qkv_gate(q, k, v, g, beta):
         _shape("g", g, (B, T, H, dk))
         gate = GDN_GATE_KEY
     dt = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    if shared_qk:
+        return B, T, H, dk, dv, dt, gate, dev, Hq
     return B, T, H, dk, dv, dt, gate, dev
 
 
@@ -210,4 +227,70 @@ def gdn_prefill_chunked(q, k, v, g, beta, state, o=None, workspace=None, chunk: 
                                        _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
                                        workspace.numel(), _stream_ptr(dev))
     _check("gdn_prefill_chunked", st)
+    return o
+
+
+def _head_map(head_map) -> int:
+    if head_map not in _HEAD_MAPS:
+        raise ValueError(f"head_map must be 'grouped' or 'tiled', got {head_map!r}")
+    return _HEAD_MAPS[head_map]
+
+
+def gdn_forward_qk_broadcast(q, k, v, g, beta, state, head_map="grouped", final_state=None,
+                             o=None):
+    """Forward with q/k [B,T,H_qk,d_k] shared by the H value heads; returns o.
+
+    head_map 'grouped': value head h reads q/k head h // (H // H_qk);
+    'tiled': q/k head h % H_qk.  state is [B,H,d_k,d_v] (one slot, in
+    place) or [B,H,K,d_k,d_v] (K snapshot slots, as gdn_forward_snapshots).
+    """
+    B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
+    hm = _head_map(head_map)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    if state.dim() == 4:
+        K = 1
+        _shape("state", state, (B, H, dk, dv))
+    elif state.dim() == 5:
+        K = state.shape[2]
+        _shape("state", state, (B, H, K, dk, dv))
+    else:
+        raise ValueError("state must be [B,H,d_k,d_v] or [B,H,K,d_k,d_v]")
+    if final_state is not None:
+        _dev_tensor("final_state", final_state, (torch.float32,), dev)
+        _shape("final_state", final_state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    st = library().gdn_forward_qk_broadcast(B, T, H, Hq, hm, dk, dv, dt, gate, K, _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                            _ptr(final_state), _ptr(o), _stream_ptr(dev))
+    _check("gdn_forward_qk_broadcast", st)
+    return o
+
+
+def gdn_prefill_chunked_qk_broadcast(q, k, v, g, beta, state, head_map="grouped", o=None,
+                                     workspace=None, chunk: int = 64):
+    """Chunked prefill with q/k [B,T,H_qk,d_k] shared by the H value heads
+    (head_map as in gdn_forward_qk_broadcast); state [B,H,d_k,d_v] in place;
+    returns o."""
+    B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
+    hm = _head_map(head_map)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    _shape("state", state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    if gate != GDN_GATE_HEAD or dt != GDN_BF16:
+        raise GdnError("gdn_prefill_chunked_qk_broadcast", 3,
+                       "chunked prefill supports GDA gates with bfloat16 q/k/v only")
+    need = gdn_prefill_workspace_size(B, T, H, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked_qk_broadcast(
+        B, T, H, Hq, hm, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(o), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
+    _check("gdn_prefill_chunked_qk_broadcast", st)
     return o

@@ -13,6 +13,13 @@ bool supported_head(int d_k, int d_v) { return d_k == d_v && (d_k == 64 || d_k =
 
 int check_launch(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// H value heads read H_qk query/key heads (H a multiple of H_qk).
+int validate_heads(int H, int H_qk, int head_map) {
+    if (H_qk < 1 || (H > 0 && H % H_qk != 0)) return GDN_ERR_SHAPE;
+    if (head_map != GDN_HEADS_GROUPED && head_map != GDN_HEADS_TILED) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
 int validate_recurrent(int B, int T, int H, int d_k, int d_v, int qkv_dtype, int gate, int K,
                        const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const float* state, const float* final_state,
@@ -35,12 +42,15 @@ int validate_recurrent(int B, int T, int H, int d_k, int d_v, int qkv_dtype, int
 
 extern "C" {
 
-int gdn_forward_snapshots(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                          int32_t qkv_dtype, int32_t gate, int32_t K, const void* q,
-                          const void* k, const void* v, const float* g, const float* beta,
-                          float* state, float* final_state, float* o, void* stream) {
+int gdn_forward_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                             int32_t d_k, int32_t d_v, int32_t qkv_dtype, int32_t gate,
+                             int32_t K, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state,
+                             float* final_state, float* o, void* stream) {
     int st = validate_recurrent(B, T, H, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
                                 final_state, o);
+    if (st != GDN_OK) return st;
+    st = validate_heads(H, H_qk, head_map);
     if (st != GDN_OK) return st;
     if (B == 0 || H == 0) return GDN_OK;
     // With no token, nothing changes unless a final_state copy is requested.
@@ -59,10 +69,22 @@ int gdn_forward_snapshots(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t 
     a.H = H;
     a.K = K;
     a.d = d_k;
+    a.Hqk = H_qk;
+    a.group = H / H_qk;
+    a.tiled = head_map == GDN_HEADS_TILED;
     a.n_snap = K > 1 ? (T < K - 1 ? T : K - 1) : 0;
     a.bf16 = qkv_dtype == GDN_BF16;
     a.kda = gate == GDN_GATE_KEY;
     return check_launch(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_forward_snapshots(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t qkv_dtype, int32_t gate, int32_t K, const void* q,
+                          const void* k, const void* v, const float* g, const float* beta,
+                          float* state, float* final_state, float* o, void* stream) {
+    return gdn_forward_qk_broadcast(B, T, H, H > 0 ? H : 1, GDN_HEADS_GROUPED, d_k, d_v,
+                                    qkv_dtype, gate, K, q, k, v, g, beta, state, final_state, o,
+                                    stream);
 }
 
 int gdn_forward(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t qkv_dtype,
@@ -89,11 +111,14 @@ size_t gdn_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, 
     return gdn::prefill_workspace_bytes(B, T, H, d_k);
 }
 
-int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                        int32_t chunk, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, float* state, float* o,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                     int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                     const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, float* state, float* o,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || T < 0 || H < 0 || chunk < 1) return GDN_ERR_SHAPE;
+    const int hs = validate_heads(H, H_qk, head_map);
+    if (hs != GDN_OK) return hs;
     const bool tokens = B > 0 && H > 0 && T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
@@ -120,14 +145,26 @@ int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_
     a.T = T;
     a.H = H;
     a.d = d_k;
+    a.Hqk = H_qk;
+    a.group = H / H_qk;
+    a.tiled = head_map == GDN_HEADS_TILED;
     return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                        int32_t chunk, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, float* state, float* o,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_prefill_chunked_qk_broadcast(B, T, H, H > 0 ? H : 1, GDN_HEADS_GROUPED, d_k, d_v,
+                                            chunk, q, k, v, g, beta, state, o, workspace,
+                                            workspace_bytes, stream);
 }
 
 const char* gdn_status_str(int status) {
     switch (status) {
         case GDN_OK: return "ok";
         case GDN_ERR_NULL: return "a required pointer is NULL";
-        case GDN_ERR_SHAPE: return "invalid size (negative B/T/H, K < 1 or chunk < 1)";
+        case GDN_ERR_SHAPE: return "invalid size (negative B/T/H, K < 1, chunk < 1 or H_qk not dividing H)";
         case GDN_ERR_UNSUPPORTED:
             return "unsupported configuration (head size, dtype, gate mode, chunk or alignment)";
         case GDN_ERR_WORKSPACE: return "prefill workspace missing, misaligned or too small";

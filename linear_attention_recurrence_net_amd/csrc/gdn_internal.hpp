@@ -8,6 +8,11 @@
 
 namespace gdn {
 
+// The q/k head that value head h reads (h / group, or h % Hqk when tiled).
+__host__ __device__ inline int qk_head(int h, int Hqk, int group, bool tiled) {
+    return tiled ? h % Hqk : h / group;
+}
+
 struct RecurrentArgs {
     const void* q;
     const void* k;
@@ -18,6 +23,9 @@ struct RecurrentArgs {
     float* final_state;  // [B,H,d,d] or nullptr
     float* o;            // [B,T,H,d]
     int B, T, H, K, d;
+    int Hqk;             // q/k heads: value head h reads q/k head qk_head(h)
+    int group;           // H / Hqk
+    bool tiled;          // qk_head(h) = tiled ? h % Hqk : h / group
     int n_snap;          // snapshot slots written: K > 1 ? min(T, K-1) : 0
     bool bf16, kda;
 };
@@ -37,6 +45,8 @@ struct PrefillArgs {
     float* o;           // [B,T,H,d]
     void* workspace;
     int B, T, H, d;
+    int Hqk, group;      // q/k heads, as in RecurrentArgs
+    bool tiled;
 };
 
 size_t prefill_workspace_bytes(int B, int T, int H, int d);

@@ -185,7 +185,7 @@ template <int D>
 __global__ void __launch_bounds__(64)
 prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const float* __restrict__ g, const float* __restrict__ beta,
-                    char* __restrict__ ws, int T, int H, int NC) {
+                    char* __restrict__ ws, int T, int H, int NC, int Hqk, int group, bool tiled) {
     using L = Ws<D>;
     constexpr int KS = L::KS;
     // A (fp32) during the solve, then the hi/lo transpose of T1 (bf16); a
@@ -205,6 +205,7 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int bh = blk / NC;
     const int b = bh / H;
     const int h = bh - b * H;
+    const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
     const int t0 = n * kC;
     const int nvalid = min(kC, T - t0);
     const int lr = lane & 15;  // MFMA row / column inside a tile
@@ -235,8 +236,8 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     // fragments of the chunk's q and k rows (zero beyond the sequence end)
-    auto row_ptr = [&](const uint16_t* base, int r) {
-        return base + ((static_cast<size_t>(b) * T + t0 + r) * H + h) * D;
+    auto row_ptr = [&](const uint16_t* base, int r) {  // q or k row t0 + r
+        return base + ((static_cast<size_t>(b) * T + t0 + r) * Hqk + hq) * D;
     };
     bf16x8 kf[4][KS];
 #pragma unroll
@@ -430,7 +431,8 @@ template <int D>
 __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
-                     float* __restrict__ o, const char* __restrict__ ws, int T, int H, int NC) {
+                     float* __restrict__ o, const char* __restrict__ ws, int T, int H, int NC,
+                     int Hqk, int group, bool tiled) {
     using L = Ws<D>;
     using M = ChainLds<D>;
     constexpr int NCB = D / 16;        // column blocks per head
@@ -664,9 +666,13 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // barrier each loader waits until only its kPer newest loads (those
         // of chunk n + 2) may be outstanding.
         const int l = wave - kStateWaves - kOutWaves;
-        const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;  // element of (b, t=0, h, 0)
-        const int row_b16 = H * D * 2;                                  // bytes per token, bf16
-        const int seq_b16 = (T - 1) * row_b16 + D * 2;  // end of the last valid row
+        const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
+        const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;     // v element (b, 0, h, 0)
+        const size_t headq0 = (static_cast<size_t>(b) * T * Hqk + hq) * D; // q/k element (b, 0, hq, 0)
+        const int row_b16 = H * D * 2;                                     // bytes per token of v
+        const int rowq_b16 = Hqk * D * 2;                                  // bytes per token of q, k
+        const int seq_b16 = (T - 1) * row_b16 + D * 2;    // end of the last valid row of v
+        const int seqq_b16 = (T - 1) * rowq_b16 + D * 2;  // and of q, k
         constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
         constexpr int kPart = (kPer + 2) / 3;
         auto load = [&](int n, int qt) {
@@ -674,9 +680,9 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const int r0 = n * kC;
             const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
             const __amdgpu_buffer_rsrc_t rk =
-                make_rsrc(k + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+                make_rsrc(k + headq0 + static_cast<size_t>(r0) * Hqk * D, seqq_b16 - r0 * rowq_b16);
             const __amdgpu_buffer_rsrc_t rq =
-                make_rsrc(q + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+                make_rsrc(q + headq0 + static_cast<size_t>(r0) * Hqk * D, seqq_b16 - r0 * rowq_b16);
             const __amdgpu_buffer_rsrc_t rv =
                 make_rsrc(v + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
 #pragma unroll
@@ -692,7 +698,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     const int p = 64 * pi + lane;  // image piece: row p / PPR, slot p % PPR
                     const int rr = p / PPR;
                     dma16(isq ? rq : rk, slot + (isq ? M::kQ : M::kK) + 1024 * pi,
-                          rr * row_b16 + 16 * ((p % PPR) ^ k_swz<D>(rr)));
+                          rr * rowq_b16 + 16 * ((p % PPR) ^ k_swz<D>(rr)));
                 } else {
                     const int jv = i - 1 - 2 * KPT;
                     const int p = 64 * jv + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
@@ -756,12 +762,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     char* ws = static_cast<char*>(a.workspace);
     hipLaunchKernelGGL(prefill_prep_kernel<D>, dim3(bh * NC), dim3(64), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.g,
-                       a.beta, ws, a.T, a.H, NC);
+                       a.beta, ws, a.T, a.H, NC, a.Hqk, a.group, a.tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(kChainThreads), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, a.T, a.H, NC);
+                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, a.T, a.H, NC, a.Hqk,
+                       a.group, a.tiled);
     return hipGetLastError();
 }
 

@@ -86,11 +86,13 @@ struct TokenRaw {
     float g[KDA ? RPL : 1];
     float beta;
 
+    // bth indexes the (sequence, token, value head) of v, g, beta; bthq the
+    // (sequence, token, q/k head) of q and k.
     __device__ __forceinline__ void load(const void* q, const void* k, const void* v,
-                                         const float* gp, const float* bp, size_t bth, int row0,
-                                         int col0, int D) {
+                                         const float* gp, const float* bp, size_t bth,
+                                         size_t bthq, int row0, int col0, int D) {
         static_assert(KW % 2 == 0, "row slices are loaded 64 or 128 bits at a time");
-        const size_t ko = bth * D + row0;
+        const size_t ko = bthq * D + row0;
         const size_t vo = bth * D + col0;
         const uint32_t* kp = reinterpret_cast<const uint32_t*>(
             static_cast<const char*>(k) + ko * (BF16 ? 2 : 4));
@@ -173,7 +175,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const float* __restrict__ g,
                  const float* __restrict__ beta, float* __restrict__ state,
                  float* __restrict__ final_state, float* __restrict__ o, int T, int H, int K,
-                 int n_snap) {
+                 int n_snap, int Hqk, int group, bool tiled) {
     constexpr int CG = kCPW / 4;     // lanes across one row segment
     constexpr int RG = kWave / CG;   // row groups
     constexpr int RPL = D / RG;      // rows held per lane
@@ -192,6 +194,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int row0 = rg * RPL;
     const int b = bh / H;
     const int h = bh - b * H;
+    const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
 
     float* slots = state + static_cast<size_t>(bh) * K * TILE;
 
@@ -203,13 +206,16 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     using Raw = TokenRaw<RPL, KDA, BF16>;
     const int n_tok = ONE ? 1 : T;
     Raw cur;
-    if (n_tok > 0) cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h, row0, col0, D);
+    if (n_tok > 0)
+        cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h,
+                 (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, D);
 
     for (int t = 0; t < n_tok; ++t) {
         const size_t bth = (static_cast<size_t>(b) * T + t) * H + h;
+        const size_t bthq = (static_cast<size_t>(b) * T + t) * Hqk + hq;
         // prefetch the next token while this one is computed
         Raw nxt;
-        if (!ONE && t + 1 < n_tok) nxt.load(q, k, v, g, beta, bth + H, row0, col0, D);
+        if (!ONE && t + 1 < n_tok) nxt.load(q, k, v, g, beta, bth + H, bthq + Hqk, row0, col0, D);
 
         float kv[RPL], qv[RPL];
         cur.unpack_kq(kv, qv);
@@ -308,11 +314,11 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
     if (a.T == 1 && a.n_snap == 0)
         hipLaunchKernelGGL((recurrent_kernel<D, KDA, BF16, true>), grid, block, 0, stream, a.q,
                            a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
-                           a.n_snap);
+                           a.n_snap, a.Hqk, a.group, a.tiled);
     else
         hipLaunchKernelGGL((recurrent_kernel<D, KDA, BF16, false>), grid, block, 0, stream, a.q,
                            a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
-                           a.n_snap);
+                           a.n_snap, a.Hqk, a.group, a.tiled);
     return hipGetLastError();
 }
 

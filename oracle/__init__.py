@@ -42,7 +42,7 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)
         i = ctypes.c_int
-        lib.oracle_gdn_forward.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.oracle_gdn_forward.argtypes = [i, i, i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp]
         lib.oracle_gdn_forward.restype = i
         lib.oracle_gdn_rollback.argtypes = [i, i, i, i, i, ip, dp]
         lib.oracle_gdn_rollback.restype = i
@@ -71,26 +71,34 @@ def num_threads() -> int:
     return _load().oracle_num_threads()
 
 
-def forward(q, k, v, g, beta, state, *, kda: bool = False, want_final: bool = False):
+def forward(q, k, v, g, beta, state, *, kda: bool = False, want_final: bool = False,
+            head_map: str = "grouped"):
     """Sequential recurrence.  ``state`` is [B,H,K,dk,dv] (slot 0 = input).
 
+    q and k may have fewer heads (H_qk, a divisor of v's H) than v; value
+    head h then reads q/k head h // (H // H_qk) (head_map 'grouped') or
+    h % H_qk ('tiled').
     Returns ``(o, state_out, final_state_or_None)``; the input arrays are
     not modified.
     """
     q = _d(q)
-    B, T, H, dk = q.shape
+    B, T, Hq, dk = q.shape
+    v = _d(v)
+    H, dv = v.shape[2], v.shape[3]
     st = np.array(state, dtype=np.float64, copy=True, order="C")
-    K, dv = st.shape[2], st.shape[4]
+    K = st.shape[2]
     if st.shape != (B, H, K, dk, dv):
         raise ValueError(f"state shape {st.shape}")
-    k = _d(k, (B, T, H, dk))
+    if head_map not in ("grouped", "tiled"):
+        raise ValueError(head_map)
+    k = _d(k, (B, T, Hq, dk))
     v = _d(v, (B, T, H, dv))
     g = _d(g, (B, T, H, dk) if kda else (B, T, H))
     beta = _d(beta, (B, T, H))
     o = np.zeros((B, T, H, dv), dtype=np.float64)
     fin = np.zeros((B, H, dk, dv), dtype=np.float64) if want_final else None
-    rc = _load().oracle_gdn_forward(B, T, H, dk, dv, K, int(kda), _p(q), _p(k), _p(v), _p(g),
-                                    _p(beta), _p(st), _p(fin), _p(o))
+    rc = _load().oracle_gdn_forward(B, T, H, Hq, int(head_map == "tiled"), dk, dv, K, int(kda),
+                                    _p(q), _p(k), _p(v), _p(g), _p(beta), _p(st), _p(fin), _p(o))
     if rc != 0:
         raise RuntimeError("oracle_gdn_forward failed")
     return o, st, fin

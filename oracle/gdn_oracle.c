@@ -34,6 +34,8 @@
  *
  * Layouts (row-major, last axis contiguous):
  *   q, k [B,T,H,dk]   v, o [B,T,H,dv]   g [B,T,H] (GDA) or [B,T,H,dk] (KDA)
+ *   (oracle_gdn_forward also takes q, k with Hqk heads shared by the H value
+ *   heads, see there)
  *   beta [B,T,H]      state [B,H,K,dk,dv]   final_state [B,H,dk,dv]
  *
  * Parity pins: every function here is pinned by the CPU tests against closed
@@ -90,12 +92,19 @@ static void token_step(int dk, int dv, int kda, double* S, const double* q, cons
  *           state after the first t tokens; slot 0 and slots above T are
  *           not written;
  *   final_state[b,h] <- S_T          when final_state is not NULL.
+ * q and k have Hqk heads ([B,T,Hqk,dk]) read by the H value heads without
+ * repeating them [P2 "models : avoid Q and K repeats when using fused GDA";
+ * "reorder v heads for linear attention to avoid expensive interleaved
+ * repeat"]: value head h reads q/k head h / (H / Hqk) when tiled == 0 (the
+ * interleaved repeat: consecutive value heads share a q/k head) and
+ * h % Hqk when tiled == 1.  Hqk == H is the plain case.
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_gdn_forward(int B, int T, int H, int dk, int dv, int K, int kda,
+int oracle_gdn_forward(int B, int T, int H, int Hqk, int tiled, int dk, int dv, int K, int kda,
                        const double* q, const double* k, const double* v, const double* g,
                        const double* beta, double* state, double* final_state, double* o) {
     if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1 || K < 1) return -1;
+    if (Hqk < 1 || H % Hqk != 0) return -1;
     const size_t tile = (size_t)dk * dv;
     int bad = 0;
 #pragma omp parallel for collapse(2) schedule(static)
@@ -111,10 +120,12 @@ int oracle_gdn_forward(int B, int T, int H, int dk, int dv, int K, int kda,
             double* w = u + dv;
             double* slots = state + ((size_t)b * H + h) * K * tile;
             memcpy(S, slots, sizeof(double) * tile);
+            const int hq = tiled ? h % Hqk : h / (H / Hqk);  /* the q/k head of value head h */
             for (int t = 0; t < T; ++t) {
                 size_t bth = ((size_t)b * T + t) * H + h;
+                size_t btq = ((size_t)b * T + t) * Hqk + hq;
                 const double* gate = kda ? g + bth * dk : g + bth;
-                token_step(dk, dv, kda, S, q + bth * dk, k + bth * dk, v + bth * dv, gate,
+                token_step(dk, dv, kda, S, q + btq * dk, k + btq * dk, v + bth * dv, gate,
                            beta[bth], o + bth * dv, u, w);
                 if (K > 1 && t + 1 <= K - 1) memcpy(slots + (size_t)(t + 1) * tile, S, sizeof(double) * tile);
             }

@@ -136,3 +136,21 @@ def test_binding_rejects_cpu_tensors(lib):
     g = torch.zeros(1, 1, 1)
     with pytest.raises(ValueError, match="GPU"):
         gdn.gdn_forward(q, q, q, g, g, torch.zeros(1, 1, 64, 64))
+
+
+def test_qk_broadcast_validation(lib):
+    fb = lib.gdn_forward_qk_broadcast
+    # B, T, H, H_qk, head_map, dk, dv, dtype, gate, K, q, k, v, g, beta, state, final, o, stream
+    assert fb(1, 1, 4, 3, 0, 64, 64, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_SHAPE  # 3 does not divide 4
+    assert fb(1, 1, 4, 0, 0, 64, 64, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_SHAPE
+    assert fb(1, 1, 4, 2, 2, 64, 64, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_UNSUP  # bad head map
+    assert fb(1, 1, 4, 2, 1, 64, 64, 1, 0, 1, N, P, P, P, P, P, N, P, None) == ERR_NULL
+    assert fb(1, 1, 4, 2, 1, 96, 96, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
+    assert fb(0, 1, 4, 2, 1, 64, 64, 1, 0, 1, P, P, P, P, P, P, N, P, None) == OK
+    pb = lib.gdn_prefill_chunked_qk_broadcast
+    big = lib.gdn_prefill_workspace_size(1, 100, 4, 128, 128, 64)
+    # B, T, H, H_qk, head_map, dk, dv, chunk, q, k, v, g, beta, state, o, ws, ws_bytes, stream
+    assert pb(1, 100, 4, 3, 0, 128, 128, 64, P, P, P, P, P, P, P, P, big, None) == ERR_SHAPE
+    assert pb(1, 100, 4, 2, 5, 128, 128, 64, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
+    assert pb(1, 100, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, N, big, None) == ERR_WS
+    assert pb(1, 0, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == OK

@@ -255,3 +255,44 @@ def test_verify_then_rollback_equals_running_accepted_prefix():
         one = [x[b:b + 1, sl] for x in args]
         _, pre, _ = oracle.forward(*one, c.f64("state")[b:b + 1, :, :1])
         assert np.array_equal(rolled[b, :, 0], pre[0, :, 0])
+
+
+# --- q/k shared between value heads (head broadcast) --------------------------
+# The definition of sharing: the result equals the plain recurrence on q and k
+# repeated to H heads -- by numpy's repeat (consecutive value heads share a
+# q/k head) or tile (value head h uses q/k head h % H_qk).  The comparison is
+# bitwise: the oracle runs the same arithmetic on the same values.
+
+
+@pytest.mark.parametrize("H,H_qk", [(6, 2), (6, 3), (4, 1)])
+@pytest.mark.parametrize("kda", [False, True])
+def test_qk_broadcast_equals_materialised_repeat(H, H_qk, kda):
+    c = gi.make_case(2, 5, H, 8, K=3, gate="kda" if kda else "gda", qkv_dtype="f32", seed=40 + H_qk,
+                     H_qk=H_qk)
+    args = dict(kda=kda, want_final=True)
+    R = H // H_qk
+    for head_map, rep in (("grouped", lambda a: np.repeat(a, R, axis=2)),
+                          ("tiled", lambda a: np.tile(a, (1, 1, R, 1)))):
+        o, st, fin = oracle.forward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("g"), c.f64("beta"),
+                                    c.f64("state"), head_map=head_map, **args)
+        o2, st2, fin2 = oracle.forward(rep(c.f64("q")), rep(c.f64("k")), c.f64("v"), c.f64("g"),
+                                       c.f64("beta"), c.f64("state"), **args)
+        assert np.array_equal(o, o2) and np.array_equal(st, st2) and np.array_equal(fin, fin2), head_map
+
+
+def test_grouped_and_tiled_orders_differ():
+    # with 2 q/k heads and 4 value heads the two orders pair heads 1 and 2
+    # differently, so the outputs of those heads must differ
+    c = gi.make_case(1, 4, 4, 8, qkv_dtype="f32", seed=5, H_qk=2)
+    a = [c.f64(n) for n in ("q", "k", "v", "g", "beta")]
+    og, _, _ = oracle.forward(*a, c.f64("state"), head_map="grouped")
+    ot, _, _ = oracle.forward(*a, c.f64("state"), head_map="tiled")
+    assert np.array_equal(og[:, :, 0], ot[:, :, 0]) and np.array_equal(og[:, :, 3], ot[:, :, 3])
+    assert not np.allclose(og[:, :, 1], ot[:, :, 1]) and not np.allclose(og[:, :, 2], ot[:, :, 2])
+
+
+def test_qk_broadcast_rejects_non_divisor():
+    c = gi.make_case(1, 2, 4, 8, qkv_dtype="f32", seed=1, H_qk=2)
+    q3 = np.repeat(c.f64("q"), 3, axis=2)[:, :, :3]  # 3 q/k heads for 4 value heads
+    with pytest.raises(RuntimeError):
+        oracle.forward(q3, q3, c.f64("v"), c.f64("g"), c.f64("beta"), c.f64("state"))
