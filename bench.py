@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "8dc1dcedbb524ecd91c237d6b724e3760faa41ffd983cb3e8652007b556f8690",
-    "fetch_kib": 33508.5625,       # median over 62 decode dispatches
-    "write_kib": 66077.5625,
+    "sha256": "684eea692babf06e36dab55bb06d90a7a541af8d246c790b81ee4a3753886dc9",
+    "fetch_kib": 33508.5,       # median over 62 decode dispatches
+    "write_kib": 66079.5,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
@@ -96,6 +96,14 @@ def recurrent_bytes(B, T, H, d, K, kda, bf16, final=False) -> int:
     n_snap = min(T, K - 1) if K > 1 else 0
     state = tile + (tile if K == 1 else n_snap * tile) + (tile if final else 0)
     return B * H * (state + T * token_bytes(d, kda, bf16))
+
+
+def broadcast_bytes(B, T, H, Hq, d, bf16=True) -> int:
+    """Decode with H value heads sharing Hq q/k heads: the state in and out
+    and v, o, g, beta per value head; q and k once per q/k head."""
+    e = 2 if bf16 else 4
+    tile = 4 * d * d
+    return B * H * (2 * tile + T * (d * e + 4 * d + 8)) + B * Hq * T * 2 * d * e
 
 
 def recurrent_flops(B, T, H, d) -> int:
@@ -228,6 +236,38 @@ def bench_decode(torch, lib, steps, warmup):
     return res
 
 
+BROADCAST_WORKLOAD = dict(name="decode GDA B=64 H=32 value heads sharing H_qk=16 q/k heads "
+                               "(grouped) d=128 T=1", B=64, T=1, H=32, H_qk=16, d_k=128)
+
+
+def bench_decode_broadcast(torch, lib, steps, warmup):
+    """Decode where two value heads share each q/k head (gdn_forward_qk_broadcast)."""
+    import gdn_inputs as gi
+    w = BROADCAST_WORKLOAD
+    case = gi.make_case(w["B"], w["T"], w["H"], w["d_k"], qkv_dtype="bf16", seed=11, H_qk=w["H_qk"])
+    d = upload_case(torch, case)
+    sets = _rotating_sets(torch, d, case, with_state_slot0=True)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def mk(s):
+        args = (case.B, case.T, case.H, case.H_qk, 0, case.d_k, case.d_v, 1, 0, 1, p(s["q"]),
+                p(s["k"]), p(s["v"]), p(s["g"]), p(s["beta"]), p(s["state"]), None, p(s["o"]))
+
+        def call(stream):
+            st = lib.gdn_forward_qk_broadcast(*args, stream)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+        return call
+    calls = [mk(s) for s in sets]
+    t = _timing(*run_timed(torch, calls, steps, warmup), steps)
+    nbytes = broadcast_bytes(case.B, case.T, case.H, case.H_qk, case.d_k)
+    gbs = nbytes / (t["us_per_launch"] * 1e-6) / 1e9
+    del sets, calls
+    torch.cuda.empty_cache()
+    return dict(workload=w["name"], bytes=nbytes, achieved_gbs=gbs, frac_of_hbm_peak=gbs / HBM_PEAK_GBS,
+                tokens_per_s=case.B * case.T / (t["us_per_launch"] * 1e-6), **t)
+
+
 def bench_verify(torch, lib, cfg, steps, warmup):
     """Speculative verify (K=4 snapshots, no final state), then rollback."""
     import gdn_inputs as gi
@@ -307,6 +347,45 @@ def bench_prefill(torch, lib, steps, warmup):
     )
 
 
+VARLEN_WORKLOAD = dict(name="prefill GDA, 8192 tokens packed as 16 sequences of mixed length "
+                            "(seeded log-uniform mix), H=16 d=128 chunk 64", total=8192, N=16, H=16,
+                       d=128, seed=21)
+
+
+def bench_prefill_varlen(torch, lib, steps, warmup):
+    """The prefill token count split into many sequences (gdn_prefill_chunked_varlen)."""
+    import gdn_inputs as gi
+    w = VARLEN_WORKLOAD
+    lens = gi.varlen_lengths(w["total"], w["N"], seed=w["seed"])
+    vc = gi.make_varlen_case(lens, w["H"], w["d"], seed=w["seed"])
+    bf = torch.bfloat16
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    q, k, v = t(vc.q, bf), t(vc.k, bf), t(vc.v, bf)
+    g, beta, st = t(vc.g), t(vc.beta), t(vc.state)
+    cu = torch.from_numpy(vc.cu_seqlens).to("cuda")
+    ws_bytes = lib.gdn_prefill_varlen_workspace_size(vc.N, vc.total, vc.H, vc.d, vc.d, 64)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((vc.total, vc.H, vc.d), device="cuda")
+    vp = lambda x: ctypes.c_void_p(x.data_ptr())
+    args = (vc.N, vc.total, vc.H, vc.H, 0, vc.d, vc.d, 64, vp(cu), vp(q), vp(k), vp(v), vp(g),
+            vp(beta), vp(st), vp(o), vp(ws), ws_bytes)
+
+    def call(stream):
+        s = lib.gdn_prefill_chunked_varlen(*args, stream)
+        if s != 0:
+            raise RuntimeError(f"libgdn status {s}")
+    tm = _timing(*run_timed(torch, [call], steps, warmup), steps)
+    sec = tm["us_per_launch"] * 1e-6
+    # per sequence: tokens as in the single-sequence prefill, plus its own state in and out
+    nb = prefill_bytes(1, vc.total, vc.H, vc.d) + (vc.N - 1) * 2 * vc.H * 4 * vc.d * vc.d
+    fl = prefill_flops(1, vc.total, vc.H, vc.d)
+    return dict(workload=w["name"], lengths=lens, bytes=nb, flops=fl,
+                tokens_per_s=vc.total / sec, achieved_gbs=nb / sec / 1e9,
+                frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS, achieved_tflops=fl / sec / 1e12,
+                frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS, workspace_bytes=int(ws_bytes),
+                **tm)
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores
 # ----------------------------------------------------------------------------
@@ -339,7 +418,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 20 device copies of 64 MiB (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "verify", "prefill", "all"], default="all",
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "broadcast", "varlen", "all"], default="all",
                     help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -380,6 +459,10 @@ def main():
             paths[f"verify_rollback_{'gda' if cfg == 2 else 'kda'}"] = r
             log(f"  verify {r['verify']['us_per_launch']:.2f} us {r['verify']['achieved_gbs']:.0f} GB/s; "
                 f"rollback {r['rollback']['us_per_launch']:.2f} us {r['rollback']['achieved_gbs']:.0f} GB/s")
+    if args.only in ("broadcast", "all"):
+        log("decode with shared q/k heads ...")
+        paths["decode_qk_broadcast_gda"] = r = bench_decode_broadcast(torch, lib, args.steps, args.warmup)
+        log(f"  {r['us_per_launch']:.2f} us/launch, {r['achieved_gbs']:.0f} GB/s")
     if args.only in ("prefill", "all"):
         log("prefill ...")
         steps = args.steps if args.only == "prefill" else max(5, args.steps // 10)
@@ -387,6 +470,13 @@ def main():
         paths["prefill_chunked_gda"] = r = bench_prefill(torch, lib, steps, warm)
         log(f"  prefill {r['us_per_launch']:.1f} us, {r['achieved_tflops']:.1f} TFLOP/s, "
             f"{r['achieved_gbs']:.0f} GB/s")
+    if args.only in ("varlen", "all"):
+        log("varlen prefill ...")
+        steps = args.steps if args.only == "varlen" else max(5, args.steps // 10)
+        warm = args.warmup if args.only == "varlen" else max(2, args.warmup // 10)
+        paths["prefill_chunked_varlen_gda"] = r = bench_prefill_varlen(torch, lib, steps, warm)
+        log(f"  varlen prefill {r['us_per_launch']:.1f} us, {r['tokens_per_s'] / 1e6:.1f} M tokens/s, "
+            f"{r['achieved_tflops']:.1f} TFLOP/s")
     if dec is None:
         print(json.dumps({"partial_run": args.only, "paths": paths}), flush=True)
         return

@@ -44,6 +44,9 @@ __all__ = [
     "bf16_from_bits",
     "WORKLOADS",
     "workload_case",
+    "VarlenCase",
+    "make_varlen_case",
+    "varlen_lengths",
 ]
 
 
@@ -199,3 +202,66 @@ def workload_case(i: int, seed: int | None = None, **override) -> Case:
     kw.pop("name")
     kw.update(override)
     return make_case(seed=i if seed is None else seed, **kw)
+
+
+@dataclasses.dataclass
+class VarlenCase:
+    """Sequences of different lengths packed along the token axis (bf16 q/k/v,
+    GDA gates).  q, k [total, H_qk, d]; v [total, H, d]; g, beta [total, H];
+    state [N, H, d, d] (one initial state per sequence); cu_seqlens [N+1]."""
+
+    lengths: list
+    H: int
+    d: int
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    state: np.ndarray
+    cu_seqlens: np.ndarray
+
+    @property
+    def N(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def total(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def H_qk(self) -> int:
+        return self.q.shape[1]
+
+    def sequence(self, i: int) -> Case:
+        """Sequence i alone as a B = 1 case (its rows of the packed arrays)."""
+        a, b = int(self.cu_seqlens[i]), int(self.cu_seqlens[i + 1])
+        st = self.state[i][None, :, None].copy()
+        return Case(1, b - a, self.H, self.d, self.d, 1, "gda", "bf16", self.q[None, a:b].copy(),
+                    self.k[None, a:b].copy(), self.v[None, a:b].copy(), self.g[None, a:b].copy(),
+                    self.beta[None, a:b].copy(), st, None)
+
+
+def make_varlen_case(lengths, H: int, d: int, *, H_qk: int | None = None, seed: int = 0) -> VarlenCase:
+    """Packed sequences with the recipe of make_case: one make_case draw over
+    all tokens (B = 1), cut at the sequence boundaries, and N initial states
+    drawn after it from the same generator stream."""
+    total = int(sum(lengths))
+    c = make_case(1, total, H, d, seed=seed, H_qk=H_qk)
+    rng = np.random.default_rng(seed + 1)
+    s0 = np.ascontiguousarray(rng.normal(0.0, 0.1, size=(len(lengths), H, d, d)), dtype=np.float32)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return VarlenCase(list(lengths), H, d, c.q[0], c.k[0], c.v[0], c.g[0], c.beta[0], s0, cu)
+
+
+def varlen_lengths(total: int, n: int, seed: int = 0, max_len: int | None = None) -> list:
+    """n seeded sequence lengths summing to ``total``: a wide mix (log-uniform
+    weights) so that short, ragged and multi-chunk sequences all occur."""
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(0.0, np.log(64.0), size=n))
+    lens = np.floor(w / w.sum() * total).astype(np.int64)
+    lens[int(np.argmax(lens))] += total - int(lens.sum())
+    if max_len is not None and lens.max() > max_len:
+        raise ValueError("length mix exceeds max_len")
+    return [int(x) for x in lens]

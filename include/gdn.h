@@ -162,6 +162,33 @@ int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_
                                      const float* g, const float* beta, float* state, float* o,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Chunked prefill of N sequences of different lengths packed along the
+ * token axis (the variable-length batches a serving engine prefills; the
+ * chunk algebra and the limits are those of gdn_prefill_chunked, with the
+ * shared q/k heads of gdn_prefill_chunked_qk_broadcast; pass H_qk = H and
+ * GDN_HEADS_GROUPED for plain heads).
+ * cu_seqlens: DEVICE int32 [N+1]; sequence i is tokens
+ *   [cu_seqlens[i], cu_seqlens[i+1]).  The host never reads it.  On the
+ *   device each offset is clamped to [0, total_T] and raised to the largest
+ *   offset before it, so malformed offsets shrink sequences (possibly to
+ *   nothing) but never overlap them or leave [0, total_T).  Output rows of
+ *   tokens outside every sequence are not written.
+ * q, k [total_T,H_qk,d_k]; v, o [total_T,H,d_v]; g, beta [total_T,H]
+ * (GDA log-gates); state [N,H,d_k,d_v] float32, one slot per sequence, in
+ * place (an empty sequence leaves its state unchanged).
+ * workspace: at least gdn_prefill_varlen_workspace_size(...) bytes, 256-byte
+ * aligned, owned by the caller.  Each sequence's result is bit-identical to
+ * gdn_prefill_chunked on that sequence alone.
+ */
+size_t gdn_prefill_varlen_workspace_size(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
+                                         int32_t d_v, int32_t chunk);
+int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_qk,
+                               int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                               const int32_t* cu_seqlens, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, float* state,
+                               float* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gdn_status_str(int status);
 

@@ -36,20 +36,22 @@ hipError_t launch_rollback(int B, int H, int K, size_t tile_elems, const int32_t
                            float* state, int32_t* err_flag, hipStream_t stream);
 
 struct PrefillArgs {
-    const void* q;  // bf16 [B,T,H,d]
+    const void* q;  // bf16 [B,T,H,d], or [total tokens, H, d] with cu_seqlens
     const void* k;
     const void* v;
     const float* g;     // [B,T,H]
     const float* beta;  // [B,T,H]
-    float* state;       // [B,H,d,d] in/out
+    float* state;       // [B,H,d,d] in/out (B = the number of sequences)
     float* o;           // [B,T,H,d]
     void* workspace;
-    int B, T, H, d;
+    const int32_t* cu_seqlens;  // device [B+1] token offsets, or nullptr: B sequences of T tokens
+    int B, T, H, d;             // with cu_seqlens: B sequences, T = total tokens
     int Hqk, group;      // q/k heads, as in RecurrentArgs
     bool tiled;
 };
 
 size_t prefill_workspace_bytes(int B, int T, int H, int d);
+size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

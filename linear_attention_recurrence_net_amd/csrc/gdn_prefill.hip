@@ -172,10 +172,97 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
 
 }  // namespace
 
+// Where the sequences lie.  Tokens are rows of [total tokens, heads, d]
+// arrays; sequence i covers tokens [start_i, start_i + len_i) and owns the
+// workspace chunks [c0_i, c0_i + nc_i) of every head (block (h, c) at
+// ws + (h * CT + c) * kBlock, CT chunks per head).  Either N sequences of T
+// tokens each (tab == nullptr), or a table of sanitised starts and chunk
+// offsets built by prefill_table_kernel from the caller's cu_seqlens.
+struct SeqGeom {
+    const int32_t* tab;  // [0, N]: first token of each sequence; [N+1, 2N+1]: first chunk
+    int N, T, NC;        // N sequences; T tokens and NC chunks each when tab == nullptr
+    int CT;              // chunk blocks per head in the workspace
+    __device__ __forceinline__ void seq(int i, int& start, int& len, int& c0, int& nc) const {
+        if (tab != nullptr) {
+            start = tab[i];
+            len = tab[i + 1] - start;
+            c0 = tab[N + 1 + i];
+            nc = tab[N + 2 + i] - c0;
+        } else {
+            start = i * T;
+            len = T;
+            c0 = i * NC;
+            nc = NC;
+        }
+    }
+    // The sequence owning chunk c, or -1 for a chunk past the last sequence's.
+    __device__ __forceinline__ int owner(int c) const {
+        if (tab == nullptr) return c / NC;
+        const int32_t* coff = tab + N + 1;
+        if (c >= coff[N]) return -1;
+        int lo = 0, hi = N - 1;  // the last i with coff[i] <= c
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (coff[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    }
+};
+
+// Bytes of the varlen table at the start of the workspace (256-byte aligned).
+static size_t table_bytes(int N) { return ((static_cast<size_t>(2 * (N + 1)) * 4 + 255) / 256) * 256; }
+
+static size_t block_bytes(int d) { return d == 128 ? Ws<128>::kBlock : Ws<64>::kBlock; }
+
 size_t prefill_workspace_bytes(int B, int T, int H, int d) {
     const size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
-    const size_t block = d == 128 ? Ws<128>::kBlock : Ws<64>::kBlock;
-    return static_cast<size_t>(B) * H * nc * block;
+    return static_cast<size_t>(B) * H * nc * block_bytes(d);
+}
+
+// Variable lengths: at most total / C + N chunks over all sequences (each
+// sequence adds at most one partial chunk), plus the table.
+size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d) {
+    const size_t ct = (static_cast<size_t>(total) + kC - 1) / kC + N;
+    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(d);
+}
+
+// ---------------------------------------------------------------------------
+// table: sanitised sequence starts and chunk offsets from cu_seqlens.  Each
+// offset is clamped to [0, total] and made non-decreasing (a running maximum),
+// so the sequences never overlap or leave [0, total) whatever the caller
+// passes; the chunk offsets are the running sum of ceil(len / C).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64)
+prefill_table_kernel(const int32_t* __restrict__ cu, int N, int total, int32_t* __restrict__ tab) {
+    const int lane = threadIdx.x;
+    int run_max = 0, run_sum = 0;  // carried across blocks of 64 offsets
+    for (int base = 0; base <= N; base += 64) {
+        const int i = base + lane;
+        int x = 0;
+        if (i <= N) x = min(max(cu[i], 0), total);
+        // inclusive running maximum of the clamped offsets
+        int m = max(x, run_max);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(m, off, 64);
+            if (lane >= off) m = max(m, y);
+        }
+        // chunks of sequence i - 1, which ends at m_i and starts at m_(i-1)
+        int prev = __shfl_up(m, 1, 64);
+        if (lane == 0) prev = run_max;
+        int c = (i >= 1 && i <= N) ? (m - prev + kC - 1) / kC : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(c, off, 64);
+            if (lane >= off) c += y;
+        }
+        if (i <= N) {
+            tab[i] = m;
+            tab[N + 1 + i] = run_sum + c;
+        }
+        run_max = __shfl(m, 63, 64);
+        run_sum += __shfl(c, 63, 64);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -185,7 +272,7 @@ template <int D>
 __global__ void __launch_bounds__(64)
 prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const float* __restrict__ g, const float* __restrict__ beta,
-                    char* __restrict__ ws, int T, int H, int NC, int Hqk, int group, bool tiled) {
+                    char* __restrict__ ws, SeqGeom geo, int H, int Hqk, int group, bool tiled) {
     using L = Ws<D>;
     constexpr int KS = L::KS;
     // A (fp32) during the solve, then the hi/lo transpose of T1 (bf16); a
@@ -200,14 +287,17 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     auto tsw = [](int r) { return 2 * ((r >> 1) & 7); };
 
     const int lane = threadIdx.x;
-    const int blk = blockIdx.x;  // (b * H + h) * NC + n
-    const int n = blk % NC;
-    const int bh = blk / NC;
-    const int b = bh / H;
-    const int h = bh - b * H;
+    const int blk = blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
+    const int h = blk / geo.CT;
+    const int c = blk - h * geo.CT;
+    const int i = geo.owner(c);
+    if (i < 0) return;  // capacity past the last sequence's chunks
+    int start, len, c0, nc;
+    geo.seq(i, start, len, c0, nc);
+    const int n = c - c0;  // chunk of sequence i
     const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
-    const int t0 = n * kC;
-    const int nvalid = min(kC, T - t0);
+    const int t0 = start + n * kC;  // first token of the chunk
+    const int nvalid = min(kC, len - n * kC);
     const int lr = lane & 15;  // MFMA row / column inside a tile
     const int grp = lane >> 4;
     char* wsb = ws + static_cast<size_t>(blk) * L::kBlock;
@@ -215,7 +305,7 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // gates: inclusive prefix sum of the log-gates over the chunk
     float gv = 0.f, bv = 0.f;
     if (lane < nvalid) {
-        const size_t bth = (static_cast<size_t>(b) * T + t0 + lane) * H + h;
+        const size_t bth = (static_cast<size_t>(t0) + lane) * H + h;
         gv = g[bth];
         bv = beta[bth];
     }
@@ -237,7 +327,7 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     // fragments of the chunk's q and k rows (zero beyond the sequence end)
     auto row_ptr = [&](const uint16_t* base, int r) {  // q or k row t0 + r
-        return base + ((static_cast<size_t>(b) * T + t0 + r) * Hqk + hq) * D;
+        return base + ((static_cast<size_t>(t0) + r) * Hqk + hq) * D;
     };
     bf16x8 kf[4][KS];
 #pragma unroll
@@ -431,7 +521,7 @@ template <int D>
 __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
-                     float* __restrict__ o, const char* __restrict__ ws, int T, int H, int NC,
+                     float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
                      int Hqk, int group, bool tiled) {
     using L = Ws<D>;
     using M = ChainLds<D>;
@@ -472,10 +562,13 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         cb = blockIdx.x % NCB;
         bh = blockIdx.x / NCB;
     }
-    const int b = bh / H;
+    const int b = bh / H;  // the sequence
     const int h = bh - b * H;
     const int col = cb * 16 + lr;
-    const char* wsh = ws + static_cast<size_t>(bh) * NC * L::kBlock;
+    int start, len, c0, NC;
+    geo.seq(b, start, len, c0, NC);
+    if (NC == 0) return;  // an empty sequence leaves its state as it is
+    const char* wsh = ws + (static_cast<size_t>(h) * geo.CT + c0) * L::kBlock;
     auto ws_rsrc = [&](int n) { return make_rsrc(wsh + static_cast<size_t>(n) * L::kBlock, L::kBlock); };
 
     if (wave < kStateWaves) {
@@ -667,12 +760,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // of chunk n + 2) may be outstanding.
         const int l = wave - kStateWaves - kOutWaves;
         const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
-        const size_t head0 = (static_cast<size_t>(b) * T * H + h) * D;     // v element (b, 0, h, 0)
-        const size_t headq0 = (static_cast<size_t>(b) * T * Hqk + hq) * D; // q/k element (b, 0, hq, 0)
-        const int row_b16 = H * D * 2;                                     // bytes per token of v
-        const int rowq_b16 = Hqk * D * 2;                                  // bytes per token of q, k
-        const int seq_b16 = (T - 1) * row_b16 + D * 2;    // end of the last valid row of v
-        const int seqq_b16 = (T - 1) * rowq_b16 + D * 2;  // and of q, k
+        const size_t head0 = (static_cast<size_t>(start) * H + h) * D;      // v element (start, h, 0)
+        const size_t headq0 = (static_cast<size_t>(start) * Hqk + hq) * D;  // q/k element (start, hq, 0)
+        const int row_b16 = H * D * 2;                                      // bytes per token of v
+        const int rowq_b16 = Hqk * D * 2;                                   // bytes per token of q, k
+        const int seq_b16 = (len - 1) * row_b16 + D * 2;    // end of the last valid row of v
+        const int seqq_b16 = (len - 1) * rowq_b16 + D * 2;  // and of q, k
         constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
         constexpr int kPart = (kPer + 2) / 3;
         auto load = [&](int n, int qt) {
@@ -731,7 +824,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // ======================= storer wavefront ==========================
         // chunk n's output block from sO to o: lane -> row lane / 4 + 16 i,
         // columns 4 (lane % 4) + 0..3 of the block, read as two 8-byte halves
-        float* const obase = o + ((static_cast<size_t>(b) * T) * H + h) * D + cb * 16 + 4 * (lane & 3);
+        float* const obase = o + (static_cast<size_t>(start) * H + h) * D + cb * 16 + 4 * (lane & 3);
         auto store_o = [&](int n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -739,8 +832,8 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 const float* src = &sO[rr][4 * (lane & 3)];
                 const f32x2 a = *reinterpret_cast<const f32x2*>(src);
                 const f32x2 c = *reinterpret_cast<const f32x2*>(src + 2);
-                const int tok = n * kC + rr;
-                if (tok < T)
+                const int tok = n * kC + rr;  // token of the sequence
+                if (tok < len)
                     *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * D) = f32x4{a[0], a[1], c[0], c[1]};
             }
         };
@@ -757,17 +850,35 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 template <int D>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    const int NC = (a.T + kC - 1) / kC;
-    const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     char* ws = static_cast<char*>(a.workspace);
-    hipLaunchKernelGGL(prefill_prep_kernel<D>, dim3(bh * NC), dim3(64), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.g,
-                       a.beta, ws, a.T, a.H, NC, a.Hqk, a.group, a.tiled);
+    SeqGeom geo;
+    if (a.cu_seqlens != nullptr) {  // variable lengths: the table first
+        geo.tab = reinterpret_cast<const int32_t*>(ws);
+        geo.N = a.B;
+        geo.T = 0;
+        geo.NC = 0;
+        geo.CT = (a.T + kC - 1) / kC + a.B;
+        hipLaunchKernelGGL(prefill_table_kernel, dim3(1), dim3(64), 0, stream, a.cu_seqlens, a.B, a.T,
+                           reinterpret_cast<int32_t*>(ws));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ws += table_bytes(a.B);
+    } else {
+        geo.tab = nullptr;
+        geo.N = a.B;
+        geo.T = a.T;
+        geo.NC = (a.T + kC - 1) / kC;
+        geo.CT = a.B * geo.NC;
+    }
+    hipLaunchKernelGGL(prefill_prep_kernel<D>, dim3(static_cast<unsigned>(a.H) * geo.CT), dim3(64), 0,
+                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(kChainThreads), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, a.T, a.H, NC, a.Hqk,
+                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, geo, a.H, a.Hqk,
                        a.group, a.tiled);
     return hipGetLastError();
 }

@@ -154,3 +154,19 @@ def test_qk_broadcast_validation(lib):
     assert pb(1, 100, 4, 2, 5, 128, 128, 64, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
     assert pb(1, 100, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, N, big, None) == ERR_WS
     assert pb(1, 0, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == OK
+
+
+def test_prefill_varlen_validation(lib):
+    wsz = lib.gdn_prefill_varlen_workspace_size
+    need = wsz(3, 300, 4, 128, 128, 64)
+    assert need >= wsz(1, 300, 4, 128, 128, 64) > 0  # more sequences, more partial chunks
+    assert wsz(3, 300, 4, 128, 128, 32) == 0
+    pv = lib.gdn_prefill_chunked_varlen
+    # N, total, H, H_qk, map, dk, dv, chunk, cu, q, k, v, g, beta, state, o, ws, ws_bytes, stream
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, N, P, P, P, P, P, P, P, P, need, None) == ERR_NULL
+    assert pv(-1, 300, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
+    assert pv(3, 300, 4, 3, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
+    assert pv(3, 300, 4, 2, 0, 128, 128, 32, P, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
+    assert pv(0, 300, 4, 2, 0, 128, 128, 64, N, P, P, P, P, P, P, P, N, 0, None) == OK
+    assert pv(3, 0, 4, 2, 0, 128, 128, 64, P, N, N, N, N, N, P, N, N, 0, None) == OK
