@@ -386,6 +386,48 @@ def bench_prefill_varlen(torch, lib, steps, warmup):
                 **tm)
 
 
+SNAP_WORKLOAD = dict(name="verify of a 16-token draft through the chunked path: GDA B=32 H=16 d=128 "
+                          "T=16, K=17 snapshots (one per token), no final state", B=32, T=16, H=16, d=128,
+                     K=17)
+
+
+def bench_prefill_snapshots(torch, lib, steps, warmup):
+    """gdn_prefill_chunked_snapshots on a long draft, with the recurrent
+    snapshot kernel timed on the same inputs beside it."""
+    import gdn_inputs as gi
+    w = SNAP_WORKLOAD
+    case = gi.make_case(w["B"], w["T"], w["H"], w["d"], K=w["K"], qkv_dtype="bf16", seed=13)
+    d = upload_case(torch, case)
+    sets = _rotating_sets(torch, d, case)
+    ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def chunked(s):
+        args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, case.K, vp(s["q"]),
+                vp(s["k"]), vp(s["v"]), vp(s["g"]), vp(s["beta"]), vp(s["state"]), None, vp(s["o"]),
+                vp(ws), ws_bytes)
+
+        def call(stream):
+            st = lib.gdn_prefill_chunked_snapshots(*args, stream)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+        return call
+    ct = _timing(*run_timed(torch, [chunked(s) for s in sets], steps, warmup), steps)
+    rec = [raw_forward_call(lib, case, s, s["state"], s["o"], K=case.K) for s in sets]
+    rt = _timing(*run_timed(torch, rec, steps, warmup), steps)
+    nb = recurrent_bytes(case.B, case.T, case.H, case.d_k, case.K, False, True)
+    tokens = case.B * case.T
+    out = dict(workload=w["name"], bytes=nb, rotating_sets=len(sets), workspace_bytes=int(ws_bytes))
+    for key, t in (("chunked", ct), ("recurrent", rt)):
+        gbs = nb / (t["us_per_launch"] * 1e-6) / 1e9
+        out[key] = dict(tokens_per_s=tokens / (t["us_per_launch"] * 1e-6), achieved_gbs=gbs,
+                        frac_of_hbm_peak=gbs / HBM_PEAK_GBS, **t)
+    del sets, rec
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores
 # ----------------------------------------------------------------------------
@@ -418,7 +460,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 20 device copies of 64 MiB (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "verify", "prefill", "broadcast", "varlen", "all"], default="all",
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "broadcast", "varlen", "snapshots", "all"], default="all",
                     help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -477,6 +519,13 @@ def main():
         paths["prefill_chunked_varlen_gda"] = r = bench_prefill_varlen(torch, lib, steps, warm)
         log(f"  varlen prefill {r['us_per_launch']:.1f} us, {r['tokens_per_s'] / 1e6:.1f} M tokens/s, "
             f"{r['achieved_tflops']:.1f} TFLOP/s")
+    if args.only in ("snapshots", "all"):
+        log("chunked verify with snapshots ...")
+        steps = args.steps if args.only == "snapshots" else max(5, args.steps // 4)
+        warm = args.warmup if args.only == "snapshots" else max(2, args.warmup // 4)
+        paths["prefill_snapshots_draft16_gda"] = r = bench_prefill_snapshots(torch, lib, steps, warm)
+        log(f"  chunked {r['chunked']['us_per_launch']:.1f} us ({r['chunked']['achieved_gbs']:.0f} GB/s), "
+            f"recurrent {r['recurrent']['us_per_launch']:.1f} us ({r['recurrent']['achieved_gbs']:.0f} GB/s)")
     if dec is None:
         print(json.dumps({"partial_run": args.only, "paths": paths}), flush=True)
         return

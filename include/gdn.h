@@ -189,6 +189,32 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
                                const void* v, const float* g, const float* beta, float* state,
                                float* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Chunked prefill that also emits state snapshots: the slot semantics of
+ * gdn_forward_snapshots (koboldcpp commit log, tag v1.113.1, bullet "metal:
+ * add GDN partial rollback") computed by the chunked path of
+ * gdn_prefill_chunked (llama.cpp commit log, tag b9752, bullet "llama :
+ * enable chunked fused GDN path"), so that a long draft can be verified by
+ * the chunked kernels and then rolled back with gdn_rollback_select.
+ * state [B,H,K,d_k,d_v] float32: slot 0 is the input and, for K > 1, is not
+ *   written; slot t (1 <= t <= min(T, K-1)) receives the state after t
+ *   tokens; slots past T are untouched.  K == 1 writes the final state back
+ *   to slot 0 (this is then exactly gdn_prefill_chunked_qk_broadcast).
+ * final_state [B,H,d_k,d_v] or NULL: for K > 1, the state after all T tokens
+ *   (with T == 0, a copy of slot 0).  Ignored when K == 1.
+ * q, k [B,T,H_qk,d_k] and head_map as in gdn_prefill_chunked_qk_broadcast;
+ * every other argument, the workspace and the limits as in
+ * gdn_prefill_chunked.  K < 1 -> GDN_ERR_SHAPE.  Outputs and snapshots are
+ * within the prefill tolerance of the token recurrence (the snapshots come
+ * from the chunk's own W rows, advanced token by token in float32).
+ */
+int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                  int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                  int32_t K, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, float* state,
+                                  float* final_state, float* o, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gdn_status_str(int status);
 

@@ -10,7 +10,8 @@ Entry points (same names as the C ABI):
   gdn_forward, gdn_forward_snapshots, gdn_rollback_select,
   gdn_prefill_workspace_size, gdn_prefill_chunked,
   gdn_forward_qk_broadcast, gdn_prefill_chunked_qk_broadcast,
-  gdn_prefill_varlen_workspace_size, gdn_prefill_chunked_varlen
+  gdn_prefill_varlen_workspace_size, gdn_prefill_chunked_varlen,
+  gdn_prefill_chunked_snapshots
 """
 
 from ._binding import (  # noqa: F401
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     gdn_forward_snapshots,
     gdn_prefill_chunked,
     gdn_prefill_chunked_qk_broadcast,
+    gdn_prefill_chunked_snapshots,
     gdn_prefill_chunked_varlen,
     gdn_prefill_varlen_workspace_size,
     gdn_prefill_workspace_size,

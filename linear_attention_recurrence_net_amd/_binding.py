@@ -26,6 +26,7 @@ EXPORTED = (
     "gdn_prefill_chunked_qk_broadcast",
     "gdn_prefill_varlen_workspace_size",
     "gdn_prefill_chunked_varlen",
+    "gdn_prefill_chunked_snapshots",
     "gdn_status_str",
 )
 
@@ -68,6 +69,8 @@ def library() -> ctypes.CDLL:
     lib.gdn_forward_qk_broadcast.argtypes = [i32] * 10 + [vp] * 9
     lib.gdn_forward_qk_broadcast.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.argtypes = [i32] * 8 + [vp] * 8 + [sz, vp]
+    lib.gdn_prefill_chunked_snapshots.argtypes = [i32] * 9 + [vp] * 9 + [sz, vp]
+    lib.gdn_prefill_chunked_snapshots.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.restype = ctypes.c_int
     lib.gdn_prefill_varlen_workspace_size.argtypes = [i32] * 6
     lib.gdn_prefill_varlen_workspace_size.restype = sz
@@ -299,6 +302,42 @@ def gdn_prefill_chunked_qk_broadcast(q, k, v, g, beta, state, head_map="grouped"
         B, T, H, Hq, hm, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(state), _ptr(o), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check("gdn_prefill_chunked_qk_broadcast", st)
+    return o
+
+
+def gdn_prefill_chunked_snapshots(q, k, v, g, beta, state, head_map="grouped", final_state=None,
+                                  o=None, workspace=None, chunk: int = 64):
+    """Chunked prefill writing state snapshots: state [B,H,K,d_k,d_v] with
+    slot 0 the input; slot t <- state after t tokens for 1 <= t <= min(T, K-1);
+    for K > 1 the final state goes to final_state [B,H,d_k,d_v] if given
+    (K == 1: back to slot 0).  q/k may have H_qk heads as in
+    gdn_prefill_chunked_qk_broadcast.  Returns o."""
+    B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
+    hm = _head_map(head_map)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    if state.dim() != 5:
+        raise ValueError("state must be [B,H,K,d_k,d_v]")
+    K = state.shape[2]
+    _shape("state", state, (B, H, K, dk, dv))
+    if final_state is not None:
+        _dev_tensor("final_state", final_state, (torch.float32,), dev)
+        _shape("final_state", final_state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    if gate != GDN_GATE_HEAD or dt != GDN_BF16:
+        raise GdnError("gdn_prefill_chunked_snapshots", 3,
+                       "chunked prefill supports GDA gates with bfloat16 q/k/v only")
+    need = gdn_prefill_workspace_size(B, T, H, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked_snapshots(
+        B, T, H, Hq, hm, dk, dv, chunk, K, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
+        _stream_ptr(dev))
+    _check("gdn_prefill_chunked_snapshots", st)
     return o
 
 

@@ -41,13 +41,15 @@ struct PrefillArgs {
     const void* v;
     const float* g;     // [B,T,H]
     const float* beta;  // [B,T,H]
-    float* state;       // [B,H,d,d] in/out (B = the number of sequences)
+    float* state;       // [B,H,K,d,d]: slot 0 in (and out when K == 1), snapshots in 1..K-1
+    float* final_state; // [B,H,d,d] or nullptr; written when K > 1
     float* o;           // [B,T,H,d]
     void* workspace;
     const int32_t* cu_seqlens;  // device [B+1] token offsets, or nullptr: B sequences of T tokens
     int B, T, H, d;             // with cu_seqlens: B sequences, T = total tokens
     int Hqk, group;      // q/k heads, as in RecurrentArgs
     bool tiled;
+    int K;               // state slots per (sequence, head)
 };
 
 size_t prefill_workspace_bytes(int B, int T, int H, int d);

@@ -70,7 +70,7 @@ struct Ws {
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
 // float offsets inside E
-constexpr int kEg = 0, kEr = 64, kEl = 128;
+constexpr int kEg = 0, kEr = 64, kEl = 128, kEs = 192;
 
 // Byte offset of A operand (row tile t, k-step ks, hi/lo hl) of lane `lane` in T1F / QKF.
 __host__ __device__ constexpr int frag_off(int t, int ks, int hl, int lane) {
@@ -323,6 +323,7 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         e[kEg + lane] = expf(G);
         e[kEr + lane] = expf(Glast - G);
         if (lane == 0) e[kEl] = expf(Glast);
+        e[kEs + lane] = expf(gv);  // the token's own decay (state snapshots)
     }
 
     // fragments of the chunk's q and k rows (zero beyond the sequence end)
@@ -522,7 +523,7 @@ __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
                      float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
-                     int Hqk, int group, bool tiled) {
+                     int Hqk, int group, bool tiled, int K, float* __restrict__ final_state) {
     using L = Ws<D>;
     using M = ChainLds<D>;
     constexpr int NCB = D / 16;        // column blocks per head
@@ -574,7 +575,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (wave < kStateWaves) {
         // ======================= state wavefronts ==========================
         const int w = wave;
-        float* st = state + static_cast<size_t>(bh) * D * D;
+        // slot 0 of the sequence's K slots holds the start state; slots
+        // 1..nsnap receive the state after that many tokens, and the final
+        // state goes back to slot 0 when K == 1, else to final_state (if given)
+        float* st = state + static_cast<size_t>(bh) * K * D * D;
+        float* fin = K == 1 ? st : (final_state ? final_state + static_cast<size_t>(bh) * D * D : nullptr);
+        const int nsnap = K > 1 ? min(len, K - 1) : 0;
         // tile mt: d_k rows SRW w + 16 mt + 4 grp + 0..3 of column `col`
         f32x4 S[SMT];
 #pragma unroll
@@ -668,6 +674,35 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
             lds_barrier();  // B3: all of W and W' are in LDS
 
+            // Snapshots inside this chunk: row r of W is token r's delta
+            // beta (v - u), so the token recurrence S <- exp(g_r) S + k_r w_r^T,
+            // run from the chunk's start state, gives the state after each
+            // token.  K image and W stay in LDS until the next chunk's B1.
+            if (n * kC < nsnap) {
+                const int rn = min(kC, nsnap - n * kC);
+                f32x4 X[SMT];
+#pragma unroll
+                for (int mt = 0; mt < SMT; ++mt) X[mt] = S[mt];
+                for (int r = 0; r < rn; ++r) {
+                    const float a = E[kEs + r];
+                    const float wv = __uint_as_float(static_cast<uint32_t>(sW[0][lr][r]) << 16) +
+                                     __uint_as_float(static_cast<uint32_t>(sW[1][lr][r]) << 16);
+                    float* dst = st + static_cast<size_t>(n * kC + r + 1) * D * D;
+#pragma unroll
+                    for (int mt = 0; mt < SMT; ++mt) {
+                        const int i0 = SRW * w + 16 * mt + 4 * grp;
+                        const u32x2 kk = *reinterpret_cast<const u32x2*>(&sK[k_at<D>(r, i0)]);
+                        const float kv[4] = {__uint_as_float(kk[0] << 16), __uint_as_float(kk[0] & 0xffff0000u),
+                                             __uint_as_float(kk[1] << 16), __uint_as_float(kk[1] & 0xffff0000u)};
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            X[mt][rr] = fmaf(kv[rr], wv, a * X[mt][rr]);
+                            dst[static_cast<size_t>(i0 + rr) * D + col] = X[mt][rr];
+                        }
+                    }
+                }
+            }
+
             // S <- exp(G_last) S + K^T W' for this wavefront's state rows
 #pragma unroll
             for (int mt = 0; mt < SMT; ++mt)
@@ -689,11 +724,13 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         }
         lds_barrier();  // final barrier, matched by every wavefront
 
+        if (fin != nullptr) {
 #pragma unroll
-        for (int mt = 0; mt < SMT; ++mt)
+            for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * D + col] = S[mt][rr];
+                for (int rr = 0; rr < 4; ++rr)
+                    fin[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * D + col] = S[mt][rr];
+        }
         return;
     }
     if (wave < kStateWaves + kOutWaves) {
@@ -879,7 +916,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(kChainThreads), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.state, a.o, ws, geo, a.H, a.Hqk,
-                       a.group, a.tiled);
+                       a.group, a.tiled, a.K, a.final_state);
     return hipGetLastError();
 }
 

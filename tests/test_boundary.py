@@ -170,3 +170,19 @@ def test_prefill_varlen_validation(lib):
     assert pv(3, 300, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
     assert pv(0, 300, 4, 2, 0, 128, 128, 64, N, P, P, P, P, P, P, P, N, 0, None) == OK
     assert pv(3, 0, 4, 2, 0, 128, 128, 64, P, N, N, N, N, N, P, N, N, 0, None) == OK
+
+
+def test_prefill_snapshots_validation(lib):
+    need = lib.gdn_prefill_workspace_size(2, 100, 4, 128, 128, 64)
+    ps = lib.gdn_prefill_chunked_snapshots
+    # B, T, H, H_qk, map, dk, dv, chunk, K, q, k, v, g, beta, state, final, o, ws, ws_bytes, stream
+    assert ps(2, 100, 4, 4, 0, 128, 128, 64, 0, P, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
+    assert ps(2, 100, 4, 3, 0, 128, 128, 64, 4, P, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
+    assert ps(2, 100, 4, 4, 0, 128, 128, 64, 4, P, P, P, P, P, N, P, P, P, need, None) == ERR_NULL
+    assert ps(2, 100, 4, 4, 0, 128, 96, 64, 4, P, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
+    assert ps(2, 100, 4, 4, 2, 128, 128, 64, 4, P, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
+    assert ps(2, 100, 4, 4, 0, 128, 128, 64, 4, P, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
+    # empty problems launch nothing; T = 0 without final_state (or with K = 1) is a no-op
+    assert ps(0, 100, 4, 4, 0, 128, 128, 64, 4, N, N, N, N, N, N, N, N, N, 0, None) == OK
+    assert ps(2, 0, 4, 4, 0, 128, 128, 64, 4, N, N, N, N, N, P, N, N, N, 0, None) == OK
+    assert ps(2, 0, 4, 4, 0, 128, 128, 64, 1, N, N, N, N, N, P, P, N, N, 0, None) == OK
