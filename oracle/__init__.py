@@ -46,7 +46,7 @@ def _load():
         lib.oracle_gdn_forward.restype = i
         lib.oracle_gdn_rollback.argtypes = [i, i, i, i, i, ip, dp]
         lib.oracle_gdn_rollback.restype = i
-        lib.oracle_gdn_chunked.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp]
+        lib.oracle_gdn_chunked.argtypes = [i, i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp]
         lib.oracle_gdn_chunked.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
@@ -116,8 +116,8 @@ def rollback(accepted, state):
     return st, n
 
 
-def chunked(q, k, v, g, beta, state, *, chunk: int = 64):
-    """Chunked (WY/UT) form, GDA.  ``state`` is [B,H,dk,dv].
+def chunked(q, k, v, g, beta, state, *, chunk: int = 64, kda: bool = False):
+    """Chunked (WY/UT) form, GDA or KDA.  ``state`` is [B,H,dk,dv].
 
     Returns ``(o, state_out)``.
     """
@@ -129,10 +129,10 @@ def chunked(q, k, v, g, beta, state, *, chunk: int = 64):
         raise ValueError(f"state shape {st.shape}")
     k = _d(k, (B, T, H, dk))
     v = _d(v, (B, T, H, dv))
-    g = _d(g, (B, T, H))
+    g = _d(g, (B, T, H, dk) if kda else (B, T, H))
     beta = _d(beta, (B, T, H))
     o = np.zeros((B, T, H, dv), dtype=np.float64)
-    rc = _load().oracle_gdn_chunked(B, T, H, dk, dv, chunk, _p(q), _p(k), _p(v), _p(g),
+    rc = _load().oracle_gdn_chunked(B, T, H, dk, dv, chunk, int(kda), _p(q), _p(k), _p(v), _p(g),
                                     _p(beta), _p(st), _p(o))
     if rc != 0:
         raise RuntimeError("oracle_gdn_chunked failed")

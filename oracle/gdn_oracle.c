@@ -176,31 +176,45 @@ static void unit_lower_solve(int n, int m, const double* A, double* R) {
 }
 
 /*
- * Chunked form of the GDA recurrence [P2 "llama : enable chunked fused GDN
+ * Chunked form of the recurrence [P2 "llama : enable chunked fused GDN
  * path"] -- the pages name the chunked path but not its algebra; this is the
  * standard WY / UT form obtained by unrolling the recurrence inside a chunk.
  * For a chunk of C tokens with start state S and in-chunk cumulative
- * log-gates G_r = g_0 + ... + g_r:
+ * log-gates G_r = g_0 + ... + g_r (GDA: one number per token; KDA: one per
+ * key row i, G_r[i], [P2 "metal : add Metal backend for
+ * GGML_OP_GATED_DELTA_NET"] for the two gate kinds):
+ *   GDA
  *   A[r][s] = beta_r exp(G_r - G_s) (k_r . k_s)          for s < r, else 0
  *   W  = (I + A)^-1 diag(beta) (V - diag(exp G) K S)     (C x dv)
  *   O  = diag(exp G) Q S + (M o Q K^T) W,   M[r][s] = exp(G_r - G_s), s <= r
  *   S <- exp(G_{C-1}) S + (diag(exp(G_{C-1} - G)) K)^T W
+ *   KDA (the decay of row i between tokens s and r is exp(G_r[i] - G_s[i]))
+ *   A[r][s] = beta_r sum_i k_r[i] k_s[i] exp(G_r[i] - G_s[i])   for s < r
+ *   W  = (I + A)^-1 diag(beta) (V - Kg S),   Kg[r][i] = k_r[i] exp(G_r[i])
+ *   O  = Qg S + QKm W,   Qg[r][i] = q_r[i] exp(G_r[i]),
+ *        QKm[r][s] = sum_i q_r[i] k_s[i] exp(G_r[i] - G_s[i])   for s <= r
+ *   S[i,:] <- exp(G_{C-1}[i]) S[i,:] + sum_s exp(G_{C-1}[i] - G_s[i]) k_s[i] W[s,:]
+ * Both follow from S_r = Gam_r S + sum_{s<=r} Gam_r Gam_s^-1 k_s w_s^T with
+ * Gam_r = diag(exp G_r) and w_s the token deltas (the rows of W).
  * T need not be a multiple of C: the final chunk is simply shorter, which
  * equals padding it with k = q = v = 0, beta = 0, g = 0.
- * state [B,H,dk,dv] is read and overwritten with S_T; o [B,T,H,dv].
- * GDA only.  Returns 0, or -1 on a bad argument.
+ * state [B,H,dk,dv] is read and overwritten with S_T; o [B,T,H,dv];
+ * g [B,T,H] (kda = 0) or [B,T,H,dk] (kda = 1).
+ * Returns 0, or -1 on a bad argument.
  */
-int oracle_gdn_chunked(int B, int T, int H, int dk, int dv, int C, const double* q,
+int oracle_gdn_chunked(int B, int T, int H, int dk, int dv, int C, int kda, const double* q,
                        const double* k, const double* v, const double* g, const double* beta,
                        double* state, double* o) {
     if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1 || C < 1) return -1;
     const size_t tile = (size_t)dk * dv;
+    const int gw = kda ? dk : 1; /* gates per token */
     int bad = 0;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; ++b) {
         for (int h = 0; h < H; ++h) {
             size_t need = tile /* S */ + (size_t)C * dk * 2 /* Kc, Qc */ + (size_t)C * dv /* W */ +
-                          (size_t)C * C * 2 /* A, QKm */ + (size_t)C /* G */ + (size_t)C * dv /* tmp */;
+                          (size_t)C * C * 2 /* A, QKm */ + (size_t)C * gw /* G */ +
+                          (size_t)C * dv /* tmp */;
             double* buf = (double*)malloc(sizeof(double) * need);
             if (!buf) {
 #pragma omp atomic write
@@ -213,19 +227,18 @@ int oracle_gdn_chunked(int B, int T, int H, int dk, int dv, int C, const double*
             double* W = Qc + (size_t)C * dk;
             double* A = W + (size_t)C * dv;
             double* QK = A + (size_t)C * C;
-            double* G = QK + (size_t)C * C;
-            double* tmp = G + C;
+            double* G = QK + (size_t)C * C; /* G[r * gw + i] */
+            double* tmp = G + (size_t)C * gw;
             double* S0 = state + ((size_t)b * H + h) * tile;
             memcpy(S, S0, sizeof(double) * tile);
             for (int t0 = 0; t0 < T; t0 += C) {
                 int n = T - t0 < C ? T - t0 : C;
                 double bet[n > 0 ? n : 1];
                 /* gather the chunk and its cumulative log-gates */
-                double acc = 0.0;
                 for (int r = 0; r < n; ++r) {
                     size_t bth = ((size_t)b * T + t0 + r) * H + h;
-                    acc += g[bth];
-                    G[r] = acc;
+                    for (int i = 0; i < gw; ++i)
+                        G[(size_t)r * gw + i] = (r > 0 ? G[(size_t)(r - 1) * gw + i] : 0.0) + g[bth * gw + i];
                     bet[r] = beta[bth];
                     memcpy(Kc + (size_t)r * dk, k + bth * dk, sizeof(double) * dk);
                     memcpy(Qc + (size_t)r * dk, q + bth * dk, sizeof(double) * dk);
@@ -234,48 +247,70 @@ int oracle_gdn_chunked(int B, int T, int H, int dk, int dv, int C, const double*
                 for (int r = 0; r < n; ++r)
                     for (int s = 0; s < n; ++s) {
                         double kk = 0.0, qk = 0.0;
-                        for (int i = 0; i < dk; ++i) {
-                            kk += Kc[(size_t)r * dk + i] * Kc[(size_t)s * dk + i];
-                            qk += Qc[(size_t)r * dk + i] * Kc[(size_t)s * dk + i];
+                        if (!kda) {
+                            for (int i = 0; i < dk; ++i) {
+                                kk += Kc[(size_t)r * dk + i] * Kc[(size_t)s * dk + i];
+                                qk += Qc[(size_t)r * dk + i] * Kc[(size_t)s * dk + i];
+                            }
+                            double m = exp(G[r] - G[s]);
+                            kk *= m;
+                            qk *= m;
+                        } else if (s <= r) {
+                            for (int i = 0; i < dk; ++i) {
+                                double m = exp(G[(size_t)r * dk + i] - G[(size_t)s * dk + i]);
+                                kk += Kc[(size_t)r * dk + i] * Kc[(size_t)s * dk + i] * m;
+                                qk += Qc[(size_t)r * dk + i] * Kc[(size_t)s * dk + i] * m;
+                            }
                         }
-                        double m = exp(G[r] - G[s]);
-                        A[r * n + s] = s < r ? bet[r] * m * kk : 0.0;
-                        QK[r * n + s] = s <= r ? m * qk : 0.0;
+                        A[r * n + s] = s < r ? bet[r] * kk : 0.0;
+                        QK[r * n + s] = s <= r ? qk : 0.0;
                     }
-                /* right-hand side diag(beta) (V - diag(exp G) K S), then solve */
+                /* right-hand side diag(beta) (V - (decayed K) S), then solve */
                 for (int r = 0; r < n; ++r) {
                     size_t bth = ((size_t)b * T + t0 + r) * H + h;
-                    double e = exp(G[r]);
                     for (int j = 0; j < dv; ++j) {
                         double ks = 0.0;
-                        for (int i = 0; i < dk; ++i) ks += Kc[(size_t)r * dk + i] * S[(size_t)i * dv + j];
-                        W[(size_t)r * dv + j] = bet[r] * (v[bth * dv + j] - e * ks);
+                        if (!kda) {
+                            for (int i = 0; i < dk; ++i) ks += Kc[(size_t)r * dk + i] * S[(size_t)i * dv + j];
+                            ks *= exp(G[r]);
+                        } else {
+                            for (int i = 0; i < dk; ++i)
+                                ks += Kc[(size_t)r * dk + i] * exp(G[(size_t)r * dk + i]) * S[(size_t)i * dv + j];
+                        }
+                        W[(size_t)r * dv + j] = bet[r] * (v[bth * dv + j] - ks);
                     }
                 }
                 unit_lower_solve(n, dv, A, W);
                 /* outputs */
                 for (int r = 0; r < n; ++r) {
                     size_t bth = ((size_t)b * T + t0 + r) * H + h;
-                    double e = exp(G[r]);
                     for (int j = 0; j < dv; ++j) {
                         double qs = 0.0;
-                        for (int i = 0; i < dk; ++i) qs += Qc[(size_t)r * dk + i] * S[(size_t)i * dv + j];
+                        if (!kda) {
+                            for (int i = 0; i < dk; ++i) qs += Qc[(size_t)r * dk + i] * S[(size_t)i * dv + j];
+                            qs *= exp(G[r]);
+                        } else {
+                            for (int i = 0; i < dk; ++i)
+                                qs += Qc[(size_t)r * dk + i] * exp(G[(size_t)r * dk + i]) * S[(size_t)i * dv + j];
+                        }
                         double intra = 0.0;
                         for (int s = 0; s <= r; ++s) intra += QK[r * n + s] * W[(size_t)s * dv + j];
-                        tmp[j] = e * qs + intra;
+                        tmp[j] = qs + intra;
                     }
                     memcpy(o + bth * dv, tmp, sizeof(double) * dv);
                 }
                 /* carry the state to the end of the chunk */
-                double gl = G[n - 1];
-                double el = exp(gl);
-                for (int i = 0; i < dk; ++i)
+                for (int i = 0; i < dk; ++i) {
+                    const int gi = kda ? i : 0;
+                    const double gl = G[(size_t)(n - 1) * gw + gi];
+                    const double el = exp(gl);
                     for (int j = 0; j < dv; ++j) {
                         double add = 0.0;
                         for (int s = 0; s < n; ++s)
-                            add += exp(gl - G[s]) * Kc[(size_t)s * dk + i] * W[(size_t)s * dv + j];
+                            add += exp(gl - G[(size_t)s * gw + gi]) * Kc[(size_t)s * dk + i] * W[(size_t)s * dv + j];
                         S[(size_t)i * dv + j] = el * S[(size_t)i * dv + j] + add;
                     }
+                }
             }
             memcpy(S0, S, sizeof(double) * tile);
             free(buf);

@@ -16,7 +16,8 @@ KDA gate applied to columns, a wrong chunk-form term) fails at least one:
   S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} + beta_t k_t v_t^T;
 * KDA with equal row gates equals GDA; a prefix split equals one run;
   outputs are linear in V from a zero state;
-* the chunked form equals the sequential form at several lengths and tails;
+* the chunked form equals the sequential form at several lengths and tails,
+  for GDA and for KDA (whose chunk form with equal row gates is GDA's);
 * rollback copies slot a to slot 0 byte for byte.
 """
 
@@ -212,6 +213,39 @@ def test_chunked_equals_sequential_prefill_shape_sample():
     args = [c.f64(n) for n in ("q", "k", "v", "g", "beta")]
     o, s, _ = oracle.forward(*args, c.f64("state"))
     oc, sc = oracle.chunked(*args, c.f64("state")[:, :, 0], chunk=64)
+    assert np.abs(oc - o).max() <= 1e-10 * np.abs(o).max()
+    assert np.abs(sc - s[:, :, 0]).max() <= 1e-10 * np.abs(s).max()
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (63, 64), (65, 64), (150, 64), (37, 8), (16, 16)])
+def test_chunked_kda_equals_sequential(T, C):
+    """KDA chunk form (per-row decays inside A, QKm, the decayed K and Q and
+    the state carry) against the KDA token loop."""
+    q, k, v, g, beta, st = _rand_case(1, T, 2, 16, gate="kda", seed=40 + T)
+    o, s, _ = oracle.forward(q, k, v, g, beta, st, kda=True)
+    oc, sc = oracle.chunked(q, k, v, g, beta, st[:, :, 0], chunk=C, kda=True)
+    assert np.abs(oc - o).max() <= 1e-10 * np.abs(o).max()
+    assert np.abs(sc - s[:, :, 0]).max() <= 1e-10 * np.abs(s).max()
+
+
+def test_chunked_kda_with_equal_row_gates_is_gda():
+    """Every key row decaying by the token's one gate is the GDA chunk form."""
+    q, k, v, g, beta, st = _rand_case(2, 100, 2, 16, seed=23)
+    gk = np.repeat(g[..., None], 16, axis=-1)
+    o1, s1 = oracle.chunked(q, k, v, g, beta, st[:, :, 0])
+    o2, s2 = oracle.chunked(q, k, v, gk, beta, st[:, :, 0], kda=True)
+    assert np.abs(o2 - o1).max() <= 1e-13 * np.abs(o1).max()
+    assert np.abs(s2 - s1).max() <= 1e-13 * np.abs(s1).max()
+
+
+def test_chunked_kda_prefill_shape_strong_decay():
+    """d = 128, chunk 64, a ragged tail, and gates about four times stronger
+    than the workload's, so that decays across a chunk reach exp(-200)."""
+    c = gi.make_case(1, 130, 2, 128, gate="kda", qkv_dtype="bf16", seed=8)
+    args = [c.f64(n) for n in ("q", "k", "v", "g", "beta")]
+    args[3] = 4.0 * args[3]
+    o, s, _ = oracle.forward(*args, c.f64("state"), kda=True)
+    oc, sc = oracle.chunked(*args, c.f64("state")[:, :, 0], chunk=64, kda=True)
     assert np.abs(oc - o).max() <= 1e-10 * np.abs(o).max()
     assert np.abs(sc - s[:, :, 0]).max() <= 1e-10 * np.abs(s).max()
 
