@@ -115,6 +115,11 @@ def prefill_bytes(B, T, H, d) -> int:
     return B * T * H * (3 * 2 * d + 8 + 4 * d) + 2 * B * H * 4 * d * d
 
 
+def prefill_kda_bytes(B, T, H, d) -> int:
+    """As prefill_bytes, with one fp32 log-gate per key row instead of one per head."""
+    return B * T * H * (3 * 2 * d + 4 * d + 4 + 4 * d) + 2 * B * H * 4 * d * d
+
+
 def prefill_flops(B, T, H, d, C=64) -> int:
     """Dense-tile MFMA work of the chunk form per head-token: 2 (5 C d + 3 d^2)."""
     return B * T * H * 2 * (5 * C * d + 3 * d * d)
@@ -428,6 +433,37 @@ def bench_prefill_snapshots(torch, lib, steps, warmup):
     return out
 
 
+def bench_prefill_kda(torch, lib, steps, warmup):
+    """The prefill workload's shape with KDA gates (gdn_prefill_chunked_kda)."""
+    import gdn_inputs as gi
+    case = gi.workload_case(4, gate="kda")
+    d = upload_case(torch, case)
+    st0 = d["state"][:, :, 0].contiguous()
+    ws_bytes = lib.gdn_prefill_kda_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, vp(d["q"]), vp(d["k"]),
+            vp(d["v"]), vp(d["g"]), vp(d["beta"]), vp(st0), vp(o), vp(ws), ws_bytes)
+
+    def call(stream):
+        s = lib.gdn_prefill_chunked_kda(*args, stream)
+        if s != 0:
+            raise RuntimeError(f"libgdn status {s}")
+    t = _timing(*run_timed(torch, [call], steps, warmup), steps)
+    sec = t["us_per_launch"] * 1e-6
+    nb = prefill_kda_bytes(case.B, case.T, case.H, case.d_k)
+    fl = prefill_flops(case.B, case.T, case.H, case.d_k)
+    return dict(
+        workload="prefill KDA B=1 T=8192 H=16 d=128 chunk 64 (the prefill workload with one "
+                 "log-gate per key row)", bytes=nb, flops=fl,
+        tokens_per_s=case.B * case.T / sec,
+        achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
+        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
+        workspace_bytes=int(ws_bytes), **t,
+    )
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores
 # ----------------------------------------------------------------------------
@@ -460,7 +496,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 20 device copies of 64 MiB (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "verify", "prefill", "broadcast", "varlen", "snapshots", "all"], default="all",
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "prefill_kda", "broadcast", "varlen", "snapshots",
+                             "all"], default="all",
                     help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -511,6 +548,13 @@ def main():
         warm = args.warmup if args.only == "prefill" else max(2, args.warmup // 10)
         paths["prefill_chunked_gda"] = r = bench_prefill(torch, lib, steps, warm)
         log(f"  prefill {r['us_per_launch']:.1f} us, {r['achieved_tflops']:.1f} TFLOP/s, "
+            f"{r['achieved_gbs']:.0f} GB/s")
+    if args.only in ("prefill_kda", "all"):
+        log("prefill KDA ...")
+        steps = args.steps if args.only == "prefill_kda" else max(5, args.steps // 10)
+        warm = args.warmup if args.only == "prefill_kda" else max(2, args.warmup // 10)
+        paths["prefill_chunked_kda"] = r = bench_prefill_kda(torch, lib, steps, warm)
+        log(f"  prefill KDA {r['us_per_launch']:.1f} us, {r['achieved_tflops']:.1f} TFLOP/s, "
             f"{r['achieved_gbs']:.0f} GB/s")
     if args.only in ("varlen", "all"):
         log("varlen prefill ...")

@@ -215,6 +215,25 @@ int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
                                   float* final_state, float* o, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Chunked prefill with KDA gates: one log-gate per key row, so that row i of
+ * the state decays by exp(g_t[i]) at token t (llama.cpp commit log, tag
+ * b9752, bullets "metal : add Metal backend for GGML_OP_GATED_DELTA_NET" for
+ * the gate kinds and "llama : enable chunked fused GDN path" for the chunked
+ * path).  Arguments as in gdn_prefill_chunked_qk_broadcast, except
+ * g [B,T,H,d_k] float32 log-gates and the workspace size, which comes from
+ * gdn_prefill_kda_workspace_size.  Within the prefill tolerance of the token
+ * recurrence while, on every key row, the log-gates of any 8 consecutive
+ * tokens sum to more than -80 (per-token decays stronger than that belong to
+ * gdn_forward_qk_broadcast, which has no such limit).
+ */
+size_t gdn_prefill_kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                      int32_t chunk);
+int gdn_prefill_chunked_kda(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                            int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, float* state,
+                            float* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gdn_status_str(int status);
 

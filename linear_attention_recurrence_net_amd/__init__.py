@@ -11,7 +11,8 @@ Entry points (same names as the C ABI):
   gdn_prefill_workspace_size, gdn_prefill_chunked,
   gdn_forward_qk_broadcast, gdn_prefill_chunked_qk_broadcast,
   gdn_prefill_varlen_workspace_size, gdn_prefill_chunked_varlen,
-  gdn_prefill_chunked_snapshots
+  gdn_prefill_chunked_snapshots, gdn_prefill_kda_workspace_size,
+  gdn_prefill_chunked_kda
 """
 
 from ._binding import (  # noqa: F401
@@ -21,7 +22,9 @@ from ._binding import (  # noqa: F401
     gdn_forward_snapshots,
     gdn_prefill_chunked,
     gdn_prefill_chunked_qk_broadcast,
+    gdn_prefill_chunked_kda,
     gdn_prefill_chunked_snapshots,
+    gdn_prefill_kda_workspace_size,
     gdn_prefill_chunked_varlen,
     gdn_prefill_varlen_workspace_size,
     gdn_prefill_workspace_size,

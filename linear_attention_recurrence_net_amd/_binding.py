@@ -27,6 +27,8 @@ EXPORTED = (
     "gdn_prefill_varlen_workspace_size",
     "gdn_prefill_chunked_varlen",
     "gdn_prefill_chunked_snapshots",
+    "gdn_prefill_kda_workspace_size",
+    "gdn_prefill_chunked_kda",
     "gdn_status_str",
 )
 
@@ -71,6 +73,10 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_chunked_qk_broadcast.argtypes = [i32] * 8 + [vp] * 8 + [sz, vp]
     lib.gdn_prefill_chunked_snapshots.argtypes = [i32] * 9 + [vp] * 9 + [sz, vp]
     lib.gdn_prefill_chunked_snapshots.restype = ctypes.c_int
+    lib.gdn_prefill_kda_workspace_size.argtypes = [i32] * 6
+    lib.gdn_prefill_kda_workspace_size.restype = sz
+    lib.gdn_prefill_chunked_kda.argtypes = [i32] * 8 + [vp] * 8 + [sz, vp]
+    lib.gdn_prefill_chunked_kda.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.restype = ctypes.c_int
     lib.gdn_prefill_varlen_workspace_size.argtypes = [i32] * 6
     lib.gdn_prefill_varlen_workspace_size.restype = sz
@@ -338,6 +344,38 @@ def gdn_prefill_chunked_snapshots(q, k, v, g, beta, state, head_map="grouped", f
         _ptr(state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
         _stream_ptr(dev))
     _check("gdn_prefill_chunked_snapshots", st)
+    return o
+
+
+def gdn_prefill_kda_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int,
+                                   chunk: int = 64) -> int:
+    return int(library().gdn_prefill_kda_workspace_size(B, T, H, d_k, d_v, chunk))
+
+
+def gdn_prefill_chunked_kda(q, k, v, g, beta, state, head_map="grouped", o=None, workspace=None,
+                            chunk: int = 64):
+    """Chunked prefill with KDA gates g [B,T,H,d_k] (one log-gate per key
+    row); q/k [B,T,H_qk,d_k] as in gdn_prefill_chunked_qk_broadcast; state
+    [B,H,d_k,d_v] in place; returns o."""
+    B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
+    hm = _head_map(head_map)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    _shape("state", state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    if gate != GDN_GATE_KEY or dt != GDN_BF16:
+        raise GdnError("gdn_prefill_chunked_kda", 3,
+                       "KDA chunked prefill takes g [B,T,H,d_k] and bfloat16 q/k/v")
+    need = gdn_prefill_kda_workspace_size(B, T, H, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked_kda(
+        B, T, H, Hq, hm, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(o), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
+    _check("gdn_prefill_chunked_kda", st)
     return o
 
 

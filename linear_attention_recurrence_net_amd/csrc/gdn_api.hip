@@ -161,6 +161,7 @@ int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;
     a.K = K;
+    a.kda = false;
     return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -214,6 +215,7 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     a.cu_seqlens = cu_seqlens;
     a.final_state = nullptr;
     a.K = 1;
+    a.kda = false;
     a.B = N;
     a.T = total_T;
     a.H = H;
@@ -231,6 +233,55 @@ int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_
     return gdn_prefill_chunked_qk_broadcast(B, T, H, H > 0 ? H : 1, GDN_HEADS_GROUPED, d_k, d_v,
                                             chunk, q, k, v, g, beta, state, o, workspace,
                                             workspace_bytes, stream);
+}
+
+size_t gdn_prefill_kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                      int32_t chunk) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    return gdn::prefill_workspace_bytes(B, T, H, d_k, true);
+}
+
+int gdn_prefill_chunked_kda(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                            int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, float* state,
+                            float* o, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || T < 0 || H < 0 || chunk < 1) return GDN_ERR_SHAPE;
+    const int hs = validate_heads(H, H_qk, head_map);
+    if (hs != GDN_OK) return hs;
+    const bool tokens = B > 0 && H > 0 && T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
+    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(state) ||
+        !aligned16(o))
+        return GDN_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) return GDN_OK;
+    if (static_cast<int64_t>(T) * H * d_k * 4 >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, true);
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return GDN_ERR_WORKSPACE;
+    gdn::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.final_state = nullptr;
+    a.o = o;
+    a.workspace = workspace;
+    a.cu_seqlens = nullptr;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.d = d_k;
+    a.Hqk = H_qk;
+    a.group = H / H_qk;
+    a.tiled = head_map == GDN_HEADS_TILED;
+    a.K = 1;
+    a.kda = true;
+    return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
 const char* gdn_status_str(int status) {

@@ -39,7 +39,7 @@ struct PrefillArgs {
     const void* q;  // bf16 [B,T,H,d], or [total tokens, H, d] with cu_seqlens
     const void* k;
     const void* v;
-    const float* g;     // [B,T,H]
+    const float* g;     // [B,T,H], or [B,T,H,d] for KDA
     const float* beta;  // [B,T,H]
     float* state;       // [B,H,K,d,d]: slot 0 in (and out when K == 1), snapshots in 1..K-1
     float* final_state; // [B,H,d,d] or nullptr; written when K > 1
@@ -50,9 +50,10 @@ struct PrefillArgs {
     int Hqk, group;      // q/k heads, as in RecurrentArgs
     bool tiled;
     int K;               // state slots per (sequence, head)
+    bool kda;            // g is [.., H, d] (one log-gate per key row)
 };
 
-size_t prefill_workspace_bytes(int B, int T, int H, int d);
+size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda = false);
 size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

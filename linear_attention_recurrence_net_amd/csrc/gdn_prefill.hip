@@ -40,6 +40,8 @@
 // whose B operand is an earlier result uses that order.
 
 #include "device_common.hpp"
+#include <type_traits>
+
 #include "gdn_internal.hpp"
 
 namespace gdn {
@@ -69,8 +71,24 @@ struct Ws {
     static constexpr int kBlock = kE + 1024;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
+// KDA (one log-gate per key row): the same T1F, QKF and gate block, then the
+// three decayed images the chain reads in place of K and Q, each row-major
+// [64][D] bf16 (rows past the end of the sequence are zero):
+//   KG  K o exp(G)            (row r, key i: k_r[i] exp(G_r[i]))
+//   QG  Q o exp(G)
+//   KD  K o exp(G_last - G)
+// and E holds fp32 exp(G_last[i]) for the D key rows.
+template <int D>
+struct WsKda : Ws<D> {
+    static constexpr int kKG = Ws<D>::kBlock;
+    static constexpr int kQG = kKG + kC * D * 2;
+    static constexpr int kKD = kQG + kC * D * 2;
+    static constexpr int kBlock = kKD + kC * D * 2;
+    static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
+};
 // float offsets inside E
 constexpr int kEg = 0, kEr = 64, kEl = 128, kEs = 192;
+constexpr int kEv = 0;  // KDA: exp(G_last[i]), i < D
 
 // Byte offset of A operand (row tile t, k-step ks, hi/lo hl) of lane `lane` in T1F / QKF.
 __host__ __device__ constexpr int frag_off(int t, int ks, int hl, int lane) {
@@ -212,18 +230,21 @@ struct SeqGeom {
 // Bytes of the varlen table at the start of the workspace (256-byte aligned).
 static size_t table_bytes(int N) { return ((static_cast<size_t>(2 * (N + 1)) * 4 + 255) / 256) * 256; }
 
-static size_t block_bytes(int d) { return d == 128 ? Ws<128>::kBlock : Ws<64>::kBlock; }
+static size_t block_bytes(int d, bool kda) {
+    if (kda) return d == 128 ? WsKda<128>::kBlock : WsKda<64>::kBlock;
+    return d == 128 ? Ws<128>::kBlock : Ws<64>::kBlock;
+}
 
-size_t prefill_workspace_bytes(int B, int T, int H, int d) {
+size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda) {
     const size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
-    return static_cast<size_t>(B) * H * nc * block_bytes(d);
+    return static_cast<size_t>(B) * H * nc * block_bytes(d, kda);
 }
 
 // Variable lengths: at most total / C + N chunks over all sequences (each
 // sequence adds at most one partial chunk), plus the table.
 size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d) {
     const size_t ct = (static_cast<size_t>(total) + kC - 1) / kC + N;
-    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(d);
+    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(d, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -268,6 +289,77 @@ prefill_table_kernel(const int32_t* __restrict__ cu, int N, int total, int32_t* 
 // ---------------------------------------------------------------------------
 // prep: one wavefront per (sequence, head, chunk)
 // ---------------------------------------------------------------------------
+// T = (I + A)^-1 diag(beta) for one chunk, from A (strict lower part, fp32,
+// in sA) and beta (sBeta), written to the workspace block as T1F; sA is
+// reused for the transpose.  Called by the whole (one-wavefront) block after
+// a barrier that publishes A.
+template <class L>
+__device__ __forceinline__ void solve_store_t1(float (*sA)[kC], const float* sBeta, char* wsb,
+                                               int lane) {
+    uint16_t (*sT)[kC][kC] = reinterpret_cast<uint16_t (*)[kC][kC]>(&sA[0][0]);
+    // 8-byte unit u of row r of the transpose is kept at unit u ^ tsw(r), so
+    // that the split-order reads below (16 rows, two units each) meet every
+    // bank once.
+    auto tsw = [](int r) { return 2 * ((r >> 1) & 7); };
+    const int lr = lane & 15;
+    const int grp = lane >> 4;
+    // T = (I + A)^-1 by forward substitution, one column per lane, in fp32,
+    // in blocks of 16 rows: first the contributions of all earlier blocks
+    // (16 independent sums), then the sequential triangle of the block.
+    float x[kC];
+#pragma unroll
+    for (int I = 0; I < kC / 16; ++I) {
+        float y[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = (16 * I + i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int s4 = 0; s4 < 16 * I; s4 += 4) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * I + i][s4]);
+                y[i] = fmaf(-av.x, x[s4], y[i]);
+                y[i] = fmaf(-av.y, x[s4 + 1], y[i]);
+                y[i] = fmaf(-av.z, x[s4 + 2], y[i]);
+                y[i] = fmaf(-av.w, x[s4 + 3], y[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = y[i];
+#pragma unroll
+            for (int s = 16 * I; s < 16 * I + i; ++s) acc = fmaf(-sA[16 * I + i][s], x[s], acc);
+            x[16 * I + i] = acc;
+        }
+    }
+
+    // T1 = T diag(beta): this lane's column, split hi/lo, transposed through
+    // LDS (A is no longer read) into split-order A operands.
+    __syncthreads();  // every read of A is done before its storage is reused
+    const float bcol = sBeta[lane];
+#pragma unroll
+    for (int r = 0; r < kC; ++r) {
+        uint32_t hi, lo;
+        split_bf16(x[r] * bcol, hi, lo);
+        const int c = 4 * ((lane >> 2) ^ tsw(r)) + (lane & 3);
+        sT[0][r][c] = static_cast<uint16_t>(hi);
+        sT[1][r][c] = static_cast<uint16_t>(lo);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const int r = 16 * t + lr;
+                const int u = 8 * ks + grp;  // 8-byte unit of columns 32 ks + 4 grp + 0..3
+                const u32x2 a = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * (u ^ tsw(r))]);
+                const u32x2 c = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * ((u + 4) ^ tsw(r))]);
+                *reinterpret_cast<u32x4*>(wsb + L::kT1F + frag_off(t, ks, hl, lane)) =
+                    u32x4{a[0], a[1], c[0], c[1]};
+            }
+}
+
 template <int D>
 __global__ void __launch_bounds__(64)
 prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -280,11 +372,6 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __shared__ __attribute__((aligned(16))) float sA[kC][kC];
     __shared__ float sG[kC];
     __shared__ float sBeta[kC];
-    uint16_t (*sT)[kC][kC] = reinterpret_cast<uint16_t (*)[kC][kC]>(&sA[0][0]);
-    // 8-byte unit u of row r of the transpose is kept at unit u ^ tsw(r), so
-    // that the split-order reads below (16 rows, two units each) meet every
-    // bank once.
-    auto tsw = [](int r) { return 2 * ((r >> 1) & 7); };
 
     const int lane = threadIdx.x;
     const int blk = blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
@@ -406,61 +493,223 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution, one column per lane, in fp32,
-    // in blocks of 16 rows: first the contributions of all earlier blocks
-    // (16 independent sums), then the sequential triangle of the block.
-    float x[kC];
+    solve_store_t1<L>(sA, sBeta, wsb, lane);
+}
+
+// ---------------------------------------------------------------------------
+// prep, KDA: the per-key-row decays enter A and QKm inside the sum over keys,
+//   A[r][s]   = beta_r sum_i k_r[i] k_s[i] exp(G_r[i] - G_s[i])   (s < r)
+//   QKm[r][s] =        sum_i q_r[i] k_s[i] exp(G_r[i] - G_s[i])   (s <= r)
+// Each factor exp(G_r - G_s) is split at a reference row m between the
+// rows, exp(G_r - G_m) exp(G_m - G_s), and the two halves scale the MFMA
+// operands: row tile mt (rows 16 mt..) uses m = 16 mt + 8 against every
+// column tile.  For columns of earlier tiles both halves are at most 1; on
+// the diagonal tile each half spans at most 8 tokens of decay, so the
+// operands stay in range while the log-gates of 8 consecutive tokens sum to
+// more than -80 on every key row.  The walk over the key axis goes in steps
+// of 32 keys, so that only 32 of the D gates per row are live at a time:
+// the cumulative gates G of the step are an inclusive scan over the chunk's
+// rows (16 lanes hold 16 rows; the totals of earlier row tiles are added).
+// ---------------------------------------------------------------------------
+
+// x + (x of the lane `off` below in the same 16-lane row; 0 for the row's
+// first `off` lanes).
+template <int off>
+__device__ __forceinline__ float add_row_shr(float x) {
+    return x + __builtin_bit_cast(
+                   float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + off, 0xf, 0xf, true));
+}
+
+// Inclusive prefix sum over the 16 lanes of each row of the wavefront.
+__device__ __forceinline__ float scan16(float x) {
+    x = add_row_shr<1>(x);
+    x = add_row_shr<2>(x);
+    x = add_row_shr<4>(x);
+    return add_row_shr<8>(x);
+}
+
+// Eight floats -> one bf16 MFMA operand (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
+    return as_bf16x8(u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])});
+}
+
+template <int D>
+__global__ void __launch_bounds__(64)
+prefill_prep_kda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                        const float* __restrict__ g, const float* __restrict__ beta,
+                        char* __restrict__ ws, SeqGeom geo, int H, int Hqk, int group, bool tiled) {
+    using L = WsKda<D>;
+    constexpr int KS = D / 32;
+    __shared__ __attribute__((aligned(16))) float sA[kC][kC];
+    __shared__ float sBeta[kC];
+
+    const int lane = threadIdx.x;
+    const int blk = blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
+    const int h = blk / geo.CT;
+    const int c = blk - h * geo.CT;
+    const int i = geo.owner(c);
+    if (i < 0) return;  // capacity past the last sequence's chunks
+    int start, len, c0, nc;
+    geo.seq(i, start, len, c0, nc);
+    const int n = c - c0;
+    const int hq = qk_head(h, Hqk, group, tiled);
+    const int t0 = start + n * kC;
+    const int nvalid = min(kC, len - n * kC);
+    const int lr = lane & 15;
+    const int grp = lane >> 4;
+    char* wsb = ws + static_cast<size_t>(blk) * L::kBlock;
+
+    sBeta[lane] = lane < nvalid ? beta[(static_cast<size_t>(t0) + lane) * H + h] : 0.f;
+
+    // pair p = mt (mt + 1) / 2 + nt of row tile mt and column tile nt <= mt
+    f32x4 accA[10], accQ[10];
 #pragma unroll
-    for (int I = 0; I < kC / 16; ++I) {
-        float y[16];
+    for (int p = 0; p < 10; ++p) {
+        accA[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accQ[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float* E = reinterpret_cast<float*>(wsb + L::kE);
+
+    // bf16 element j of 8 packed in a u32x4
+    auto elem = [](const u32x4& w, int j) {
+        return __uint_as_float((j & 1) ? (w[j >> 1] & 0xffff0000u) : (w[j >> 1] << 16));
+    };
+#pragma unroll 1
+    for (int ks = 0; ks < KS; ++ks) {
+        // this lane: keys d0 + 0..7 of rows 16 t + lr
+        const int d0 = 32 * ks + 8 * grp;
+        float G[4][8];
+        u32x4 kb[4], qb[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = (16 * I + i == lane) ? 1.f : 0.f;
+        for (int t = 0; t < 4; ++t) {
+            const int r = 16 * t + lr;
+            if (r < nvalid) {
+                const size_t tok = static_cast<size_t>(t0) + r;
+                const f32x4 g0 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * D + d0);
+                const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * D + d0 + 4);
+                kb[t] = *reinterpret_cast<const u32x4*>(k + (tok * Hqk + hq) * D + d0);
+                qb[t] = *reinterpret_cast<const u32x4*>(q + (tok * Hqk + hq) * D + d0);
 #pragma unroll
-        for (int s4 = 0; s4 < 16 * I; s4 += 4) {
+                for (int j = 0; j < 4; ++j) {
+                    G[t][j] = g0[j];
+                    G[t][4 + j] = g1[j];
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * I + i][s4]);
-                y[i] = fmaf(-av.x, x[s4], y[i]);
-                y[i] = fmaf(-av.y, x[s4 + 1], y[i]);
-                y[i] = fmaf(-av.z, x[s4 + 2], y[i]);
-                y[i] = fmaf(-av.w, x[s4 + 3], y[i]);
+                for (int j = 0; j < 8; ++j) G[t][j] = 0.f;
+                kb[t] = u32x4{0u, 0u, 0u, 0u};
+                qb[t] = u32x4{0u, 0u, 0u, 0u};
             }
         }
+        // cumulative gates over the chunk's rows
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = y[i];
+        for (int j = 0; j < 8; ++j) {
+            float carry = 0.f;
 #pragma unroll
-            for (int s = 16 * I; s < 16 * I + i; ++s) acc = fmaf(-sA[16 * I + i][s], x[s], acc);
-            x[16 * I + i] = acc;
+            for (int t = 0; t < 4; ++t) {
+                G[t][j] = scan16(G[t][j]) + carry;
+                carry = __shfl(G[t][j], (lane & 48) | 15, 64);  // through the tile's last row
+            }
+        }
+        float GL[8];  // G at the chunk's last row (rows past the sequence add 0)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) GL[j] = __shfl(G[3][j], (lane & 48) | 15, 64);
+
+        // A and QKm contributions of these 32 keys
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            float ref[8], x[8], y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ref[j] = __shfl(G[mt][j], (lane & 48) | 8, 64);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = __expf(G[mt][j] - ref[j]);
+                x[j] = elem(kb[mt], j) * e;
+                y[j] = elem(qb[mt], j) * e;
+            }
+            const bf16x8 a = pack8(x);
+            const bf16x8 qa = pack8(y);
+#pragma unroll
+            for (int nt = 0; nt <= mt; ++nt) {
+                float z[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) z[j] = elem(kb[nt], j) * __expf(ref[j] - G[nt][j]);
+                const bf16x8 b = pack8(z);
+                const int p = mt * (mt + 1) / 2 + nt;
+                accA[p] = mfma(a, b, accA[p]);   // rows 16 mt + 4 grp + .., column 16 nt + lr
+                accQ[p] = mfma(b, qa, accQ[p]);  // transposed: row 16 mt + lr, columns 16 nt + 4 grp + ..
+            }
+        }
+
+        // the decayed images for the chain
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float a[8], b[8], d[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float eg = __expf(G[t][j]);
+                a[j] = elem(kb[t], j) * eg;
+                b[j] = elem(qb[t], j) * eg;
+                d[j] = elem(kb[t], j) * __expf(GL[j] - G[t][j]);
+            }
+            const size_t off = (static_cast<size_t>(16 * t + lr) * D + d0) * 2;
+            *reinterpret_cast<bf16x8*>(wsb + L::kKG + off) = pack8(a);
+            *reinterpret_cast<bf16x8*>(wsb + L::kQG + off) = pack8(b);
+            *reinterpret_cast<bf16x8*>(wsb + L::kKD + off) = pack8(d);
+        }
+        if (lr == 0) {
+            float el[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) el[j] = __expf(GL[j]);
+            *reinterpret_cast<f32x4*>(E + kEv + d0) = f32x4{el[0], el[1], el[2], el[3]};
+            *reinterpret_cast<f32x4*>(E + kEv + d0 + 4) = f32x4{el[4], el[5], el[6], el[7]};
         }
     }
+    __syncthreads();  // sBeta
 
-    // T1 = T diag(beta): this lane's column, split hi/lo, transposed through
-    // LDS (A is no longer read) into split-order A operands.
-    __syncthreads();  // every read of A is done before its storage is reused
-    const float bcol = sBeta[lane];
+    // A (strict lower part, rows scaled by beta) to LDS
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-        uint32_t hi, lo;
-        split_bf16(x[r] * bcol, hi, lo);
-        const int c = 4 * ((lane >> 2) ^ tsw(r)) + (lane & 3);
-        sT[0][r][c] = static_cast<uint16_t>(hi);
-        sT[1][r][c] = static_cast<uint16_t>(lo);
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt <= mt; ++nt) {
+            const f32x4 acc = accA[mt * (mt + 1) / 2 + nt];
+            const int col = 16 * nt + lr;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 16 * mt + 4 * grp + rr;
+                sA[row][col] = col < row ? sBeta[row] * acc[rr] : 0.f;
+            }
+        }
+
+    // QKm (diagonal included) as hi/lo A operands in split k order, as for GDA
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + lr;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x2 hi[2], lo[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int st = 2 * ks + half;
+                const int s0 = 16 * st + 4 * grp;
+                hi[half] = u32x2{0u, 0u};
+                lo[half] = u32x2{0u, 0u};
+                if (st <= rt) {
+                    const f32x4 acc = accQ[rt * (rt + 1) / 2 + st];
+                    float x[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[j] = (s0 + j <= r) ? acc[j] : 0.f;
+                    split4(x[0], x[1], x[2], x[3], hi[half], lo[half]);
+                }
+            }
+            *reinterpret_cast<u32x4*>(wsb + L::kQKF + frag_off(rt, ks, 0, lane)) =
+                u32x4{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+            *reinterpret_cast<u32x4*>(wsb + L::kQKF + frag_off(rt, ks, 1, lane)) =
+                u32x4{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+        }
     }
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                const int r = 16 * t + lr;
-                const int u = 8 * ks + grp;  // 8-byte unit of columns 32 ks + 4 grp + 0..3
-                const u32x2 a = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * (u ^ tsw(r))]);
-                const u32x2 c = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * ((u + 4) ^ tsw(r))]);
-                *reinterpret_cast<u32x4*>(wsb + L::kT1F + frag_off(t, ks, hl, lane)) =
-                    u32x4{a[0], a[1], c[0], c[1]};
-            }
+    solve_store_t1<L>(sA, sBeta, wsb, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,35 +746,43 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
 // the others compute on chunk n.  Operands that one wavefront reads alone
 // and that the workspace holds in fragment order (its T1 or QKm rows) go
 // straight from memory to its registers.
-template <int D>
+// KDA: the K and Q images are the decayed images KG and QG of the
+// workspace, and a third image, KD, is the K^T operand of the state update.
+// With three images at D = 128 three slots exceed the LDS, so KDA at D = 128
+// keeps two slots and loads one chunk ahead.
+template <int D, bool KDA>
 struct ChainLds {
+    static constexpr int kImages = KDA ? 3 : 2;
     static constexpr int kE = 0;                           // gate block (Ws<D>::kE layout)
-    static constexpr int kK = kE + 1024;                   // K image
-    static constexpr int kQ = kK + kC * D * 2;             // Q image
-    static constexpr int kV = kQ + kC * D * 2;             // V block, [64][16] bf16
+    static constexpr int kK = kE + 1024;                   // K image (KDA: KG)
+    static constexpr int kQ = kK + kC * D * 2;             // Q image (KDA: QG)
+    static constexpr int kKD = kQ + kC * D * 2;            // KDA: KD image
+    static constexpr int kV = kK + kImages * kC * D * 2;   // V block, [64][16] bf16
     static constexpr int kSlot = kV + kC * 16 * 2;
-    static constexpr int kLoads = 1 + 2 * (kC * D * 2 / 1024) + 2;  // 1 KiB loads per chunk
+    static constexpr int kLoads = 1 + kImages * (kC * D * 2 / 1024) + 2;  // 1 KiB loads per chunk
+    static constexpr int kRing = (KDA && D == 128) ? 2 : 3;
+    static constexpr int kAhead = kRing - 1;  // chunks loaded ahead of the one in use
 };
 
 constexpr int kStateWaves = 4;   // chunk rows 16 w.., state rows (d_k / 4) w..
 constexpr int kOutWaves = 4;     // chunk rows 16 w.. of the output
 constexpr int kLoadWaves = 2;
 constexpr int kChainThreads = 64 * (kStateWaves + kOutWaves + kLoadWaves + 1);  // + the storer
-constexpr int kRing = 3;
 
 // Two 8-byte LDS reads -> one split-order operand (k = c + 0..3 and c + 16 + 0..3).
 __device__ __forceinline__ bf16x8 ld_split(const uint16_t* p0, const uint16_t* p1) {
     return join(*reinterpret_cast<const u32x2*>(p0), *reinterpret_cast<const u32x2*>(p1));
 }
 
-template <int D>
+template <int D, bool KDA>
 __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
                      float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
                      int Hqk, int group, bool tiled, int K, float* __restrict__ final_state) {
-    using L = Ws<D>;
-    using M = ChainLds<D>;
+    using L = std::conditional_t<KDA, WsKda<D>, Ws<D>>;
+    using M = ChainLds<D, KDA>;
+    constexpr int kRing = M::kRing;
     constexpr int NCB = D / 16;        // column blocks per head
     constexpr int KS = L::KS;          // k-steps over d_k
     constexpr int SRW = D / 4;         // state rows per state wavefront
@@ -610,6 +867,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int n = 0; n < NC; ++n) {
             const char* slot = sL[n % kRing];
             const uint16_t* sK = reinterpret_cast<const uint16_t*>(slot + M::kK);
+            const uint16_t* sKT = reinterpret_cast<const uint16_t*>(slot + (KDA ? M::kKD : M::kK));
             const uint16_t* sV = reinterpret_cast<const uint16_t*>(slot + M::kV);
             const float* E = reinterpret_cast<const float*>(slot + M::kE);
             lds_barrier();  // B1: chunk n's operands and start state are in LDS
@@ -623,12 +881,24 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 X = mfma(ld_split(&sK[k_at<D>(r, c)], &sK[k_at<D>(r, c + 16)]),
                          ld_split(&sS[lr][c], &sS[lr][c + 16]), X);
             }
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
-            const f32x4 er = *reinterpret_cast<const f32x4*>(&E[kEr + 16 * w + 4 * grp]);
-            const float el = E[kEl];
+            // GDA: exp(G_r) for the rows of X, exp(G_last - G_r) for W', and
+            // exp(G_last) for S; KDA: exp(G_last[i]) for this wavefront's state rows
+            f32x4 eg = {1.f, 1.f, 1.f, 1.f}, er = {1.f, 1.f, 1.f, 1.f};
+            float el = 1.f;
+            f32x4 egl[SMT];
+            if constexpr (KDA) {
+#pragma unroll
+                for (int mt = 0; mt < SMT; ++mt)
+                    egl[mt] = *reinterpret_cast<const f32x4*>(&E[kEv + SRW * w + 16 * mt + 4 * grp]);
+            } else {
+                eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
+                er = *reinterpret_cast<const f32x4*>(&E[kEr + 16 * w + 4 * grp]);
+                el = E[kEl];
+            }
             const u32x2 vv = ld_tr(&sV[(16 * w + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3)]);
 
-            // R = V - exp(G) X for this wavefront's rows, hi/lo to LDS
+            // R = V - exp(G) X (KDA: V - X, the decay is inside KG) for this
+            // wavefront's rows, hi/lo to LDS
             {
                 u32x2 rh, rl;
                 split4(__uint_as_float(vv[0] << 16) - eg[0] * X[0],
@@ -661,16 +931,18 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 for (int ks = 0; ks < 2; ++ks) {
                     const int r = 32 * ks + 4 * grp + (lr >> 2);
                     const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
-                    kt[mt][ks] = join(ld_tr(&sK[k_at<D>(r, cc)]), ld_tr(&sK[k_at<D>(r + 16, cc)]));
+                    kt[mt][ks] = join(ld_tr(&sKT[k_at<D>(r, cc)]), ld_tr(&sKT[k_at<D>(r + 16, cc)]));
                 }
             {
                 u32x2 wh, wl, ph, pl;
                 split4(W, wh, wl);
-                split4(er[0] * W[0], er[1] * W[1], er[2] * W[2], er[3] * W[3], ph, pl);
                 *reinterpret_cast<u32x2*>(&sW[0][lr][16 * w + 4 * grp]) = wh;
                 *reinterpret_cast<u32x2*>(&sW[1][lr][16 * w + 4 * grp]) = wl;
-                *reinterpret_cast<u32x2*>(&sWp[0][lr][16 * w + 4 * grp]) = ph;
-                *reinterpret_cast<u32x2*>(&sWp[1][lr][16 * w + 4 * grp]) = pl;
+                if constexpr (!KDA) {  // KDA: the decay to the chunk end is inside KD
+                    split4(er[0] * W[0], er[1] * W[1], er[2] * W[2], er[3] * W[3], ph, pl);
+                    *reinterpret_cast<u32x2*>(&sWp[0][lr][16 * w + 4 * grp]) = ph;
+                    *reinterpret_cast<u32x2*>(&sWp[1][lr][16 * w + 4 * grp]) = pl;
+                }
             }
             lds_barrier();  // B3: all of W and W' are in LDS
 
@@ -678,7 +950,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             // beta (v - u), so the token recurrence S <- exp(g_r) S + k_r w_r^T,
             // run from the chunk's start state, gives the state after each
             // token.  K image and W stay in LDS until the next chunk's B1.
-            if (n * kC < nsnap) {
+            if (!KDA && n * kC < nsnap) {
                 const int rn = min(kC, nsnap - n * kC);
                 f32x4 X[SMT];
 #pragma unroll
@@ -704,15 +976,17 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
 
             // S <- exp(G_last) S + K^T W' for this wavefront's state rows
+            // (KDA: S[i,:] <- exp(G_last[i]) S[i,:] + KD^T W)
 #pragma unroll
             for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= el;
+                for (int rr = 0; rr < 4; ++rr) S[mt][rr] *= KDA ? egl[mt][rr] : el;
+            uint16_t (*const sU)[16][CLD] = KDA ? sW : sWp;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int c = 32 * ks + 4 * grp;
-                const bf16x8 ph = ld_split(&sWp[0][lr][c], &sWp[0][lr][c + 16]);
-                const bf16x8 pl = ld_split(&sWp[1][lr][c], &sWp[1][lr][c + 16]);
+                const bf16x8 ph = ld_split(&sU[0][lr][c], &sU[0][lr][c + 16]);
+                const bf16x8 pl = ld_split(&sU[1][lr][c], &sU[1][lr][c + 16]);
 #pragma unroll
                 for (int mt = 0; mt < SMT; ++mt) {
                     S[mt] = mfma(kt[mt][ks], ph, S[mt]);
@@ -761,7 +1035,8 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 P = mfma(ld_split(&sQ[k_at<D>(rq, c)], &sQ[k_at<D>(rq, c + 16)]),
                          ld_split(&sS[lr][c], &sS[lr][c + 16]), P);
             }
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
+            f32x4 eg = {1.f, 1.f, 1.f, 1.f};  // KDA: the decay is inside QG
+            if constexpr (!KDA) eg = *reinterpret_cast<const f32x4*>(&E[kEg + 16 * w + 4 * grp]);
             lds_barrier();  // B2
             lds_barrier();  // B3: W is in LDS
             // O = exp(G) P + QKm W
@@ -792,9 +1067,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // Each loader issues the same number of 1 KiB direct-to-LDS loads per
         // chunk (kPer, the last one repeated where the count does not
         // divide), in three parts, one after each barrier.  The loads of
-        // chunk n + 2 go out during chunk n, and before chunk n + 1's first
-        // barrier each loader waits until only its kPer newest loads (those
-        // of chunk n + 2) may be outstanding.
+        // chunk n + kAhead go out during chunk n, and before chunk n + 1's
+        // first barrier each loader waits until chunk n + 1's loads are done
+        // (with kAhead = 2, only its kPer newest loads, those of chunk n + 2,
+        // may stay outstanding).  With two slots (kAhead = 1) slot (n + 1) % 2
+        // is reused after chunk n's first barrier: every read of chunk n - 1's
+        // slot happens before chunk n - 1's third barrier.
         const int l = wave - kStateWaves - kOutWaves;
         const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
         const size_t head0 = (static_cast<size_t>(start) * H + h) * D;      // v element (start, h, 0)
@@ -822,34 +1100,42 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 const int i = min(kPer * l + j, M::kLoads - 1);
                 if (i == 0) {
                     dma16(rw, slot + M::kE, L::kE + 16 * lane);
-                } else if (i < 1 + 2 * KPT) {
-                    const bool isq = i >= 1 + KPT;  // K image pieces, then Q image pieces
-                    const int pi = i - 1 - (isq ? KPT : 0);
+                } else if (i < 1 + M::kImages * KPT) {
+                    const int im = (i - 1) / KPT;  // image: K (KG), Q (QG), then KD
+                    const int pi = i - 1 - im * KPT;
                     const int p = 64 * pi + lane;  // image piece: row p / PPR, slot p % PPR
                     const int rr = p / PPR;
-                    dma16(isq ? rq : rk, slot + (isq ? M::kQ : M::kK) + 1024 * pi,
-                          rr * rowq_b16 + 16 * ((p % PPR) ^ k_swz<D>(rr)));
+                    const int piece = 16 * ((p % PPR) ^ k_swz<D>(rr));
+                    char* dst = slot + M::kK + im * (kC * D * 2) + 1024 * pi;
+                    if constexpr (KDA) {  // the workspace's row-major images
+                        const int src = im == 0 ? L::kKG : (im == 1 ? L::kQG : L::kKD);
+                        dma16(rw, dst, src + rr * (D * 2) + piece);
+                    } else {
+                        dma16(im == 1 ? rq : rk, dst, rr * rowq_b16 + piece);
+                    }
                 } else {
-                    const int jv = i - 1 - 2 * KPT;
+                    const int jv = i - 1 - M::kImages * KPT;
                     const int p = 64 * jv + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
                     dma16(rv, slot + M::kV + 1024 * jv, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
                 }
             }
         };
-        for (int qt = 0; qt < 3; ++qt) load(0, qt);
-        if (NC > 1)
-            for (int qt = 0; qt < 3; ++qt) load(1, qt);
+        constexpr int A = M::kAhead;
+        for (int a = 0; a < A; ++a)
+            if (a < NC)
+                for (int qt = 0; qt < 3; ++qt) load(a, qt);
         vm_wait_all();
         for (int n = 0; n < NC; ++n) {
-            const bool more = n + 2 < NC;  // slot (n + 2) % 3 was last read before B1
+            const bool more = n + A < NC;  // slot (n + A) % kRing was last read before B1
             lds_barrier();  // B1
-            if (more) load(n + 2, 0);
+            if (more) load(n + A, 0);
             lds_barrier();  // B2
-            if (more) load(n + 2, 1);
+            if (more) load(n + A, 1);
             lds_barrier();  // B3
             if (more) {
-                load(n + 2, 2);
-                vm_wait_keep<kPer>();  // chunk n + 1's loads are done
+                load(n + A, 2);
+                if constexpr (A == 2) vm_wait_keep<kPer>();  // chunk n + 1's loads are done
+                else vm_wait_all();
             } else {
                 vm_wait_all();
             }
@@ -885,7 +1171,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D>
+template <int D, bool KDA>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     char* ws = static_cast<char*>(a.workspace);
     SeqGeom geo;
@@ -907,21 +1193,28 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         geo.NC = (a.T + kC - 1) / kC;
         geo.CT = a.B * geo.NC;
     }
-    hipLaunchKernelGGL(prefill_prep_kernel<D>, dim3(static_cast<unsigned>(a.H) * geo.CT), dim3(64), 0,
-                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
+    const dim3 prep_grid(static_cast<unsigned>(a.H) * geo.CT);
+    const auto* q = static_cast<const uint16_t*>(a.q);
+    const auto* k = static_cast<const uint16_t*>(a.k);
+    if (KDA)
+        hipLaunchKernelGGL(prefill_prep_kda_kernel<D>, prep_grid, dim3(64), 0, stream, q, k, a.g,
+                           a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
+    else
+        hipLaunchKernelGGL(prefill_prep_kernel<D>, prep_grid, dim3(64), 0, stream, q, k, a.g, a.beta,
+                           ws, geo, a.H, a.Hqk, a.group, a.tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
-    hipLaunchKernelGGL(prefill_chain_kernel<D>, dim3(bh * (D / 16)), dim3(kChainThreads), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.state, a.o, ws, geo, a.H, a.Hqk,
-                       a.group, a.tiled, a.K, a.final_state);
+    hipLaunchKernelGGL((prefill_chain_kernel<D, KDA>), dim3(bh * (D / 16)), dim3(kChainThreads), 0,
+                       stream, q, k, static_cast<const uint16_t*>(a.v), a.state, a.o, ws, geo, a.H,
+                       a.Hqk, a.group, a.tiled, a.K, a.final_state);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-    return a.d == 128 ? launch_prefill_t<128>(a, stream) : launch_prefill_t<64>(a, stream);
+    if (a.kda)
+        return a.d == 128 ? launch_prefill_t<128, true>(a, stream) : launch_prefill_t<64, true>(a, stream);
+    return a.d == 128 ? launch_prefill_t<128, false>(a, stream) : launch_prefill_t<64, false>(a, stream);
 }
 
 }  // namespace gdn

@@ -186,3 +186,19 @@ def test_prefill_snapshots_validation(lib):
     assert ps(0, 100, 4, 4, 0, 128, 128, 64, 4, N, N, N, N, N, N, N, N, N, 0, None) == OK
     assert ps(2, 0, 4, 4, 0, 128, 128, 64, 4, N, N, N, N, N, P, N, N, N, 0, None) == OK
     assert ps(2, 0, 4, 4, 0, 128, 128, 64, 1, N, N, N, N, N, P, P, N, N, 0, None) == OK
+
+
+def test_prefill_kda_validation(lib):
+    wsz = lib.gdn_prefill_kda_workspace_size
+    need = wsz(1, 100, 4, 128, 128, 64)
+    assert need > lib.gdn_prefill_workspace_size(1, 100, 4, 128, 128, 64) > 0  # three more images
+    assert wsz(1, 100, 4, 128, 128, 32) == 0
+    pk = lib.gdn_prefill_chunked_kda
+    # B, T, H, H_qk, map, dk, dv, chunk, q, k, v, g, beta, state, o, ws, ws_bytes, stream
+    assert pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, N, P, P, P, P, need, None) == ERR_NULL
+    assert pk(1, 100, 4, 3, 0, 128, 128, 64, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
+    assert pk(1, 100, 4, 4, 0, 128, 128, 16, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
+    assert pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, ctypes.c_void_p(260), P, P, P, P, need,
+              None) == ERR_UNSUP
+    assert pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
+    assert pk(1, 0, 4, 4, 0, 128, 128, 64, N, N, N, N, N, P, N, N, 0, None) == OK
