@@ -71,19 +71,21 @@ struct Ws {
     static constexpr int kBlock = kE + 1024;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
-// KDA (one log-gate per key row): the same T1F, QKF and gate block, then the
-// three decayed images the chain reads in place of K and Q, each row-major
-// [64][D] bf16 (rows past the end of the sequence are zero):
-//   KG  K o exp(G)            (row r, key i: k_r[i] exp(G_r[i]))
-//   QG  Q o exp(G)
-//   KD  K o exp(G_last - G)
+// KDA (one log-gate per key row): the same T1F, QKF and gate block, then
+// the decayed operands the chain reads in place of K and Q (rows past the end
+// of the sequence are zero):
+//   KG   K o exp(G), row-major [64][D] bf16 (row r, key i: k_r[i] exp(G_r[i]))
+//   QG   Q o exp(G), the same layout
+//   KDF  (K o exp(G_last - G))^T as the state update's A operands: for state
+//        wavefront w, state tile mt and k-step ks (chunk rows 32 ks.., split
+//        order), 64 lanes x 16 bytes at ((w * D/64 + mt) * 2 + ks) * 1 KiB
 // and E holds fp32 exp(G_last[i]) for the D key rows.
 template <int D>
 struct WsKda : Ws<D> {
     static constexpr int kKG = Ws<D>::kBlock;
     static constexpr int kQG = kKG + kC * D * 2;
-    static constexpr int kKD = kQG + kC * D * 2;
-    static constexpr int kBlock = kKD + kC * D * 2;
+    static constexpr int kKDF = kQG + kC * D * 2;
+    static constexpr int kBlock = kKDF + kC * D * 2;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
 // float offsets inside E
@@ -569,6 +571,10 @@ prefill_prep_kda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         accQ[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float* E = reinterpret_cast<float*>(wsb + L::kE);
+    // sA is free until A is formed: the transpose of one step's K o exp(G_last - G),
+    // [32 keys][64 rows] bf16, rows padded to 72 so that the fragment reads
+    // (16 keys x 8 bytes) meet distinct banks
+    uint16_t (*sKT)[72] = reinterpret_cast<uint16_t (*)[72]>(&sA[0][0]);
 
     // bf16 element j of 8 packed in a u32x4
     auto elem = [](const u32x4& w, int j) {
@@ -641,21 +647,38 @@ prefill_prep_kda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
             }
         }
 
-        // the decayed images for the chain
+        // the decayed images for the chain; K o exp(G_last - G) goes through
+        // sKT (the key-major transpose of this step's 32 keys) into the state
+        // update's operand fragments
+        __syncthreads();  // the previous step's reads of sKT are done
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            float a[8], b[8], d[8];
+            float a[8], b[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float eg = __expf(G[t][j]);
                 a[j] = elem(kb[t], j) * eg;
                 b[j] = elem(qb[t], j) * eg;
-                d[j] = elem(kb[t], j) * __expf(GL[j] - G[t][j]);
+                const float dk = elem(kb[t], j) * __expf(GL[j] - G[t][j]);
+                sKT[8 * grp + j][16 * t + lr] = static_cast<uint16_t>(cvt2(dk, 0.f) & 0xffffu);
             }
             const size_t off = (static_cast<size_t>(16 * t + lr) * D + d0) * 2;
             *reinterpret_cast<bf16x8*>(wsb + L::kKG + off) = pack8(a);
             *reinterpret_cast<bf16x8*>(wsb + L::kQG + off) = pack8(b);
-            *reinterpret_cast<bf16x8*>(wsb + L::kKD + off) = pack8(d);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k16 = 0; k16 < 2; ++k16) {  // keys 32 ks + 16 k16 + lr
+            const int i0 = 32 * ks + 16 * k16;
+            const int w = i0 / (D / 4), mt = (i0 % (D / 4)) / 16;  // the state wavefront and tile
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                const uint16_t* src = &sKT[16 * k16 + lr][32 * ks2 + 4 * grp];
+                const u32x2 lo4 = *reinterpret_cast<const u32x2*>(src);
+                const u32x2 hi4 = *reinterpret_cast<const u32x2*>(src + 16);
+                *reinterpret_cast<u32x4*>(wsb + L::kKDF + ((((w * (D / 64) + mt) * 2 + ks2) * 64 + lane) * 16)) =
+                    u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+            }
         }
         if (lr == 0) {
             float el[8];
@@ -747,20 +770,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
 // and that the workspace holds in fragment order (its T1 or QKm rows) go
 // straight from memory to its registers.
 // KDA: the K and Q images are the decayed images KG and QG of the
-// workspace, and a third image, KD, is the K^T operand of the state update.
-// With three images at D = 128 three slots exceed the LDS, so KDA at D = 128
-// keeps two slots and loads one chunk ahead.
+// workspace (the state update's K^T operand goes from the workspace straight
+// to the state wavefronts' registers).
 template <int D, bool KDA>
 struct ChainLds {
-    static constexpr int kImages = KDA ? 3 : 2;
+    static constexpr int kImages = 2;
     static constexpr int kE = 0;                           // gate block (Ws<D>::kE layout)
     static constexpr int kK = kE + 1024;                   // K image (KDA: KG)
     static constexpr int kQ = kK + kC * D * 2;             // Q image (KDA: QG)
-    static constexpr int kKD = kQ + kC * D * 2;            // KDA: KD image
     static constexpr int kV = kK + kImages * kC * D * 2;   // V block, [64][16] bf16
     static constexpr int kSlot = kV + kC * 16 * 2;
     static constexpr int kLoads = 1 + kImages * (kC * D * 2 / 1024) + 2;  // 1 KiB loads per chunk
-    static constexpr int kRing = (KDA && D == 128) ? 2 : 3;
+    static constexpr int kRing = 3;
     static constexpr int kAhead = kRing - 1;  // chunks loaded ahead of the one in use
 };
 
@@ -862,12 +883,23 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     t1[ks][hl] = as_bf16x8(buf_ld16(rw, L::kT1F + frag_off(w, ks, hl, lane)));
         };
         load_t1(0);
+        bf16x8 kt[SMT][2];
+        // KDA: the state update's K^T operands, in fragment order in the workspace
+        auto load_kt = [&](int n) {
+            const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
+#pragma unroll
+            for (int mt = 0; mt < SMT; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    kt[mt][ks] = as_bf16x8(
+                        buf_ld16(rw, WsKda<D>::kKDF + (((w * SMT + mt) * 2 + ks) * 64 + lane) * 16));
+        };
+        if constexpr (KDA) load_kt(0);
         publish_state();
 
         for (int n = 0; n < NC; ++n) {
             const char* slot = sL[n % kRing];
             const uint16_t* sK = reinterpret_cast<const uint16_t*>(slot + M::kK);
-            const uint16_t* sKT = reinterpret_cast<const uint16_t*>(slot + (KDA ? M::kKD : M::kK));
             const uint16_t* sV = reinterpret_cast<const uint16_t*>(slot + M::kV);
             const float* E = reinterpret_cast<const float*>(slot + M::kE);
             lds_barrier();  // B1: chunk n's operands and start state are in LDS
@@ -923,16 +955,18 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
             load_t1(min(n + 1, NC - 1));  // t1 is not read again in this chunk
             // K^T operands of the state update (d_k rows SRW w + 16 mt + l%16,
-            // chunk rows in split order), read while W forms
-            bf16x8 kt[SMT][2];
+            // chunk rows in split order), read while W forms (KDA: loaded
+            // during the previous chunk)
+            if constexpr (!KDA) {
 #pragma unroll
-            for (int mt = 0; mt < SMT; ++mt)
+                for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int r = 32 * ks + 4 * grp + (lr >> 2);
-                    const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
-                    kt[mt][ks] = join(ld_tr(&sKT[k_at<D>(r, cc)]), ld_tr(&sKT[k_at<D>(r + 16, cc)]));
-                }
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const int r = 32 * ks + 4 * grp + (lr >> 2);
+                        const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
+                        kt[mt][ks] = join(ld_tr(&sK[k_at<D>(r, cc)]), ld_tr(&sK[k_at<D>(r + 16, cc)]));
+                    }
+            }
             {
                 u32x2 wh, wl, ph, pl;
                 split4(W, wh, wl);
@@ -993,6 +1027,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     S[mt] = mfma(kt[mt][ks], pl, S[mt]);
                 }
             }
+            if constexpr (KDA) load_kt(min(n + 1, NC - 1));  // kt is not read again in this chunk
             // sS was last read before B2 (by every wavefront)
             publish_state();
         }
@@ -1067,12 +1102,10 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // Each loader issues the same number of 1 KiB direct-to-LDS loads per
         // chunk (kPer, the last one repeated where the count does not
         // divide), in three parts, one after each barrier.  The loads of
-        // chunk n + kAhead go out during chunk n, and before chunk n + 1's
-        // first barrier each loader waits until chunk n + 1's loads are done
-        // (with kAhead = 2, only its kPer newest loads, those of chunk n + 2,
-        // may stay outstanding).  With two slots (kAhead = 1) slot (n + 1) % 2
-        // is reused after chunk n's first barrier: every read of chunk n - 1's
-        // slot happens before chunk n - 1's third barrier.
+        // chunk n + kAhead (= 2) go out during chunk n, and before chunk
+        // n + 1's first barrier each loader waits until chunk n + 1's loads are
+        // done: only its kPer newest loads, those of chunk n + 2, may stay
+        // outstanding.
         const int l = wave - kStateWaves - kOutWaves;
         const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
         const size_t head0 = (static_cast<size_t>(start) * H + h) * D;      // v element (start, h, 0)
@@ -1101,15 +1134,14 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 if (i == 0) {
                     dma16(rw, slot + M::kE, L::kE + 16 * lane);
                 } else if (i < 1 + M::kImages * KPT) {
-                    const int im = (i - 1) / KPT;  // image: K (KG), Q (QG), then KD
+                    const int im = (i - 1) / KPT;  // image: K (KG), then Q (QG)
                     const int pi = i - 1 - im * KPT;
                     const int p = 64 * pi + lane;  // image piece: row p / PPR, slot p % PPR
                     const int rr = p / PPR;
                     const int piece = 16 * ((p % PPR) ^ k_swz<D>(rr));
                     char* dst = slot + M::kK + im * (kC * D * 2) + 1024 * pi;
                     if constexpr (KDA) {  // the workspace's row-major images
-                        const int src = im == 0 ? L::kKG : (im == 1 ? L::kQG : L::kKD);
-                        dma16(rw, dst, src + rr * (D * 2) + piece);
+                        dma16(rw, dst, (im == 0 ? L::kKG : L::kQG) + rr * (D * 2) + piece);
                     } else {
                         dma16(im == 1 ? rq : rk, dst, rr * rowq_b16 + piece);
                     }
