@@ -433,6 +433,37 @@ def bench_prefill_snapshots(torch, lib, steps, warmup):
     return out
 
 
+def bench_prefill_f32(torch, lib, steps, warmup):
+    """The prefill workload with float32 q/k/v (gdn_prefill_chunked_ex; rounded
+    to bf16 inside the kernels for the MFMA products)."""
+    import gdn_inputs as gi
+    case = gi.workload_case(4, qkv_dtype="f32")
+    d = upload_case(torch, case)
+    st0 = d["state"][:, :, 0].contiguous()
+    ws_bytes = lib.gdn_prefill_workspace_size_ex(case.B, case.T, case.H, case.d_k, case.d_v, 64, 0, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, 0, 0, 1, vp(d["q"]), vp(d["k"]),
+            vp(d["v"]), vp(d["g"]), vp(d["beta"]), vp(st0), None, vp(o), vp(ws), ws_bytes)
+
+    def call(stream):
+        s = lib.gdn_prefill_chunked_ex(*args, stream)
+        if s != 0:
+            raise RuntimeError(f"libgdn status {s}")
+    t = _timing(*run_timed(torch, [call], steps, warmup), steps)
+    sec = t["us_per_launch"] * 1e-6
+    B, T, H, dd = case.B, case.T, case.H, case.d_k
+    nb = B * T * H * (3 * 4 * dd + 8 + 4 * dd) + 2 * B * H * 4 * dd * dd
+    fl = prefill_flops(B, T, H, dd)
+    return dict(
+        workload="prefill GDA B=1 T=8192 H=16 d=128 chunk 64 with float32 q/k/v", bytes=nb, flops=fl,
+        tokens_per_s=B * T / sec, achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
+        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
+        workspace_bytes=int(ws_bytes), **t,
+    )
+
+
 def bench_prefill_kda(torch, lib, steps, warmup):
     """The prefill workload's shape with KDA gates (gdn_prefill_chunked_kda)."""
     import gdn_inputs as gi
@@ -496,8 +527,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 20 device copies of 64 MiB (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "verify", "prefill", "prefill_kda", "broadcast", "varlen", "snapshots",
-                             "all"], default="all",
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "prefill_kda", "prefill_f32", "broadcast", "varlen",
+                             "snapshots", "all"], default="all",
                     help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -556,6 +587,12 @@ def main():
         paths["prefill_chunked_kda"] = r = bench_prefill_kda(torch, lib, steps, warm)
         log(f"  prefill KDA {r['us_per_launch']:.1f} us, {r['achieved_tflops']:.1f} TFLOP/s, "
             f"{r['achieved_gbs']:.0f} GB/s")
+    if args.only in ("prefill_f32", "all"):
+        log("prefill with float32 q/k/v ...")
+        steps = args.steps if args.only == "prefill_f32" else max(5, args.steps // 10)
+        warm = args.warmup if args.only == "prefill_f32" else max(2, args.warmup // 10)
+        paths["prefill_chunked_f32_inputs"] = r = bench_prefill_f32(torch, lib, steps, warm)
+        log(f"  prefill f32 inputs {r['us_per_launch']:.1f} us, {r['achieved_tflops']:.1f} TFLOP/s")
     if args.only in ("varlen", "all"):
         log("varlen prefill ...")
         steps = args.steps if args.only == "varlen" else max(5, args.steps // 10)

@@ -234,6 +234,32 @@ int gdn_prefill_chunked_kda(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32
                             const void* v, const float* g, const float* beta, float* state,
                             float* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The general chunked prefill: every choice the specialised prefill entry
+ * points fix, as arguments (llama.cpp commit log, tag b9752, bullets
+ * "metal : add Metal backend for GGML_OP_GATED_DELTA_NET" -- GDA or KDA,
+ * head sizes 64 and 128 -- and "llama : enable chunked fused GDN path").
+ * qkv_dtype: GDN_BF16, or GDN_F32 -- q, k and v float32, rounded to bf16 for
+ *   the MFMA products (round to nearest even), so that the result is the
+ *   bf16 path's on the rounded inputs and within the prefill tolerance of
+ *   the token recurrence on the float32 inputs.
+ * gate: GDN_GATE_HEAD (g [B,T,H]) or GDN_GATE_KEY (g [B,T,H,d_k], the range
+ *   stated for gdn_prefill_chunked_kda).
+ * K, state, final_state: as in gdn_prefill_chunked_snapshots; KDA takes
+ *   K == 1 only (GDN_ERR_UNSUPPORTED otherwise).
+ * q, k [B,T,H_qk,d_k] and head_map as in gdn_prefill_chunked_qk_broadcast;
+ * v, o, beta as in gdn_prefill_chunked.  The workspace holds at least
+ * gdn_prefill_workspace_size_ex(...) bytes (larger for KDA and for float32
+ * inputs), 256-byte aligned, owned by the caller.
+ */
+size_t gdn_prefill_workspace_size_ex(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                     int32_t chunk, int32_t qkv_dtype, int32_t gate);
+int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                           int32_t d_k, int32_t d_v, int32_t chunk, int32_t qkv_dtype, int32_t gate,
+                           int32_t K, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, float* final_state, float* o,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gdn_status_str(int status);
 

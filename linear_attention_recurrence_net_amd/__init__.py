@@ -12,7 +12,7 @@ Entry points (same names as the C ABI):
   gdn_forward_qk_broadcast, gdn_prefill_chunked_qk_broadcast,
   gdn_prefill_varlen_workspace_size, gdn_prefill_chunked_varlen,
   gdn_prefill_chunked_snapshots, gdn_prefill_kda_workspace_size,
-  gdn_prefill_chunked_kda
+  gdn_prefill_chunked_kda, gdn_prefill_workspace_size_ex, gdn_prefill_chunked_ex
 """
 
 from ._binding import (  # noqa: F401
@@ -22,12 +22,14 @@ from ._binding import (  # noqa: F401
     gdn_forward_snapshots,
     gdn_prefill_chunked,
     gdn_prefill_chunked_qk_broadcast,
+    gdn_prefill_chunked_ex,
     gdn_prefill_chunked_kda,
     gdn_prefill_chunked_snapshots,
     gdn_prefill_kda_workspace_size,
     gdn_prefill_chunked_varlen,
     gdn_prefill_varlen_workspace_size,
     gdn_prefill_workspace_size,
+    gdn_prefill_workspace_size_ex,
     gdn_rollback_select,
     library,
     library_path,

@@ -29,6 +29,8 @@ EXPORTED = (
     "gdn_prefill_chunked_snapshots",
     "gdn_prefill_kda_workspace_size",
     "gdn_prefill_chunked_kda",
+    "gdn_prefill_workspace_size_ex",
+    "gdn_prefill_chunked_ex",
     "gdn_status_str",
 )
 
@@ -77,6 +79,10 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_kda_workspace_size.restype = sz
     lib.gdn_prefill_chunked_kda.argtypes = [i32] * 8 + [vp] * 8 + [sz, vp]
     lib.gdn_prefill_chunked_kda.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_size_ex.argtypes = [i32] * 8
+    lib.gdn_prefill_workspace_size_ex.restype = sz
+    lib.gdn_prefill_chunked_ex.argtypes = [i32] * 11 + [vp] * 9 + [sz, vp]
+    lib.gdn_prefill_chunked_ex.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.restype = ctypes.c_int
     lib.gdn_prefill_varlen_workspace_size.argtypes = [i32] * 6
     lib.gdn_prefill_varlen_workspace_size.restype = sz
@@ -376,6 +382,48 @@ def gdn_prefill_chunked_kda(q, k, v, g, beta, state, head_map="grouped", o=None,
         B, T, H, Hq, hm, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(state), _ptr(o), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check("gdn_prefill_chunked_kda", st)
+    return o
+
+
+def gdn_prefill_workspace_size_ex(B: int, T: int, H: int, d_k: int, d_v: int, chunk: int = 64,
+                                  qkv_dtype: int = GDN_BF16, gate: int = GDN_GATE_HEAD) -> int:
+    return int(library().gdn_prefill_workspace_size_ex(B, T, H, d_k, d_v, chunk, qkv_dtype, gate))
+
+
+def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_state=None, o=None,
+                           workspace=None, chunk: int = 64):
+    """The general chunked prefill: q/k/v bfloat16 or float32 (rounded to
+    bf16 for the MFMA products), g [B,T,H] (GDA) or [B,T,H,d_k] (KDA),
+    q/k with H_qk heads (head_map), state [B,H,d_k,d_v] (in place) or
+    [B,H,K,d_k,d_v] (K slots as in gdn_prefill_chunked_snapshots; KDA: K = 1),
+    final_state for K > 1.  Returns o."""
+    B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
+    hm = _head_map(head_map)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    if state.dim() == 4:
+        K = 1
+        _shape("state", state, (B, H, dk, dv))
+    elif state.dim() == 5:
+        K = state.shape[2]
+        _shape("state", state, (B, H, K, dk, dv))
+    else:
+        raise ValueError("state must be [B,H,d_k,d_v] or [B,H,K,d_k,d_v]")
+    if final_state is not None:
+        _dev_tensor("final_state", final_state, (torch.float32,), dev)
+        _shape("final_state", final_state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    need = gdn_prefill_workspace_size_ex(B, T, H, dk, dv, chunk, dt, gate)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked_ex(
+        B, T, H, Hq, hm, dk, dv, chunk, dt, gate, K, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
+        _stream_ptr(dev))
+    _check("gdn_prefill_chunked_ex", st)
     return o
 
 

@@ -111,12 +111,19 @@ size_t gdn_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, 
     return gdn::prefill_workspace_bytes(B, T, H, d_k);
 }
 
-int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
-                                  int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
-                                  int32_t K, const void* q, const void* k, const void* v,
-                                  const float* g, const float* beta, float* state,
-                                  float* final_state, float* o, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+size_t gdn_prefill_workspace_size_ex(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                     int32_t chunk, int32_t qkv_dtype, int32_t gate) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    if ((qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) || (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY))
+        return 0;
+    return gdn::prefill_workspace_bytes(B, T, H, d_k, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
+}
+
+int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                           int32_t d_k, int32_t d_v, int32_t chunk, int32_t qkv_dtype, int32_t gate,
+                           int32_t K, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, float* final_state, float* o,
+                           void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || T < 0 || H < 0 || chunk < 1 || K < 1) return GDN_ERR_SHAPE;
     const int hs = validate_heads(H, H_qk, head_map);
     if (hs != GDN_OK) return hs;
@@ -124,21 +131,27 @@ int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
     if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o) ||
-        (final_state && !aligned16(final_state)))
+    if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
+    // KDA snapshots would need every token's per-row decay inside the chain
+    if (gate == GDN_GATE_KEY && K > 1) return GDN_ERR_UNSUPPORTED;
+    // (KDA reads g in 16-byte pieces; GDA reads it as single floats)
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (gate == GDN_GATE_KEY && !aligned16(g)) ||
+        !aligned16(state) || !aligned16(o) || (final_state && !aligned16(final_state)))
         return GDN_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return GDN_OK;
     if (T == 0) {
         // no token: only a requested final_state copy of slot 0 remains, which
         // is exactly the recurrent entry point's T = 0 case
         if (K == 1 || final_state == nullptr) return GDN_OK;
-        return gdn_forward_qk_broadcast(B, 0, H, H_qk, head_map, d_k, d_v, GDN_BF16, GDN_GATE_HEAD,
-                                        K, nullptr, nullptr, nullptr, nullptr, nullptr, state,
+        return gdn_forward_qk_broadcast(B, 0, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K,
+                                        nullptr, nullptr, nullptr, nullptr, nullptr, state,
                                         final_state, nullptr, stream);
     }
     // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
     if (static_cast<int64_t>(T) * H * d_k * 4 >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
-    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k);
+    const bool kda = gate == GDN_GATE_KEY, f32 = qkv_dtype == GDN_F32;
+    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, kda, f32);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_WORKSPACE;
@@ -161,8 +174,20 @@ int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;
     a.K = K;
-    a.kda = false;
+    a.kda = kda;
+    a.f32 = f32;
     return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                  int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                  int32_t K, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, float* state,
+                                  float* final_state, float* o, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return gdn_prefill_chunked_ex(B, T, H, H_qk, head_map, d_k, d_v, chunk, GDN_BF16, GDN_GATE_HEAD,
+                                  K, q, k, v, g, beta, state, final_state, o, workspace,
+                                  workspace_bytes, stream);
 }
 
 int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk,
@@ -216,6 +241,7 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     a.final_state = nullptr;
     a.K = 1;
     a.kda = false;
+    a.f32 = false;
     a.B = N;
     a.T = total_T;
     a.H = H;
@@ -237,51 +263,16 @@ int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_
 
 size_t gdn_prefill_kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                       int32_t chunk) {
-    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
-    return gdn::prefill_workspace_bytes(B, T, H, d_k, true);
+    return gdn_prefill_workspace_size_ex(B, T, H, d_k, d_v, chunk, GDN_BF16, GDN_GATE_KEY);
 }
 
 int gdn_prefill_chunked_kda(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
                             int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k,
                             const void* v, const float* g, const float* beta, float* state,
                             float* o, void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 0 || T < 0 || H < 0 || chunk < 1) return GDN_ERR_SHAPE;
-    const int hs = validate_heads(H, H_qk, head_map);
-    if (hs != GDN_OK) return hs;
-    const bool tokens = B > 0 && H > 0 && T > 0;
-    if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-    if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
-    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(state) ||
-        !aligned16(o))
-        return GDN_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || T == 0) return GDN_OK;
-    if (static_cast<int64_t>(T) * H * d_k * 4 >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
-    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, true);
-    if (workspace == nullptr || workspace_bytes < need ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return GDN_ERR_WORKSPACE;
-    gdn::PrefillArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.state = state;
-    a.final_state = nullptr;
-    a.o = o;
-    a.workspace = workspace;
-    a.cu_seqlens = nullptr;
-    a.B = B;
-    a.T = T;
-    a.H = H;
-    a.d = d_k;
-    a.Hqk = H_qk;
-    a.group = H / H_qk;
-    a.tiled = head_map == GDN_HEADS_TILED;
-    a.K = 1;
-    a.kda = true;
-    return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+    return gdn_prefill_chunked_ex(B, T, H, H_qk, head_map, d_k, d_v, chunk, GDN_BF16, GDN_GATE_KEY, 1,
+                                  q, k, v, g, beta, state, nullptr, o, workspace, workspace_bytes,
+                                  stream);
 }
 
 const char* gdn_status_str(int status) {

@@ -36,7 +36,7 @@ hipError_t launch_rollback(int B, int H, int K, size_t tile_elems, const int32_t
                            float* state, int32_t* err_flag, hipStream_t stream);
 
 struct PrefillArgs {
-    const void* q;  // bf16 [B,T,H,d], or [total tokens, H, d] with cu_seqlens
+    const void* q;  // bf16 or f32 [B,T,H,d], or [total tokens, H, d] with cu_seqlens
     const void* k;
     const void* v;
     const float* g;     // [B,T,H], or [B,T,H,d] for KDA
@@ -51,9 +51,10 @@ struct PrefillArgs {
     bool tiled;
     int K;               // state slots per (sequence, head)
     bool kda;            // g is [.., H, d] (one log-gate per key row)
+    bool f32;            // q, k, v are float32 (else bf16)
 };
 
-size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda = false);
+size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda = false, bool f32 = false);
 size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

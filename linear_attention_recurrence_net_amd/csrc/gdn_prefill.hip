@@ -88,6 +88,21 @@ struct WsKda : Ws<D> {
     static constexpr int kBlock = kKDF + kC * D * 2;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
+// Workspace block of one (sequence, head, chunk) for each gate kind and input
+// type.  With float32 q/k/v the prep also rounds the chunk's K, Q and V rows
+// to bf16 images, row-major [64][D] (zero past the sequence end), which the
+// chain reads in place of the inputs; KDA's decayed KG and QG already are
+// such images, so KDA adds only V.
+template <int D, bool KDA, bool F32>
+struct WsL : std::conditional_t<KDA, WsKda<D>, Ws<D>> {
+    using Base = std::conditional_t<KDA, WsKda<D>, Ws<D>>;
+    static constexpr int kImg = kC * D * 2;
+    static constexpr int kKI = KDA ? WsKda<D>::kKG : Base::kBlock;        // K image the chain reads
+    static constexpr int kQI = KDA ? WsKda<D>::kQG : Base::kBlock + kImg; // Q image the chain reads
+    static constexpr int kVI = Base::kBlock + (KDA ? 0 : 2 * kImg);        // V image (F32)
+    static constexpr int kBlock = F32 ? kVI + kImg : Base::kBlock;
+    static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
+};
 // float offsets inside E
 constexpr int kEg = 0, kEr = 64, kEl = 128, kEs = 192;
 constexpr int kEv = 0;  // KDA: exp(G_last[i]), i < D
@@ -232,21 +247,25 @@ struct SeqGeom {
 // Bytes of the varlen table at the start of the workspace (256-byte aligned).
 static size_t table_bytes(int N) { return ((static_cast<size_t>(2 * (N + 1)) * 4 + 255) / 256) * 256; }
 
-static size_t block_bytes(int d, bool kda) {
-    if (kda) return d == 128 ? WsKda<128>::kBlock : WsKda<64>::kBlock;
-    return d == 128 ? Ws<128>::kBlock : Ws<64>::kBlock;
+template <bool KDA, bool F32>
+static size_t block_bytes_t(int d) {
+    return d == 128 ? WsL<128, KDA, F32>::kBlock : WsL<64, KDA, F32>::kBlock;
+}
+static size_t block_bytes(int d, bool kda, bool f32) {
+    if (kda) return f32 ? block_bytes_t<true, true>(d) : block_bytes_t<true, false>(d);
+    return f32 ? block_bytes_t<false, true>(d) : block_bytes_t<false, false>(d);
 }
 
-size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda) {
+size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda, bool f32) {
     const size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
-    return static_cast<size_t>(B) * H * nc * block_bytes(d, kda);
+    return static_cast<size_t>(B) * H * nc * block_bytes(d, kda, f32);
 }
 
 // Variable lengths: at most total / C + N chunks over all sequences (each
 // sequence adds at most one partial chunk), plus the table.
 size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d) {
     const size_t ct = (static_cast<size_t>(total) + kC - 1) / kC + N;
-    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(d, false);
+    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(d, false, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,12 +381,45 @@ __device__ __forceinline__ void solve_store_t1(float (*sA)[kC], const float* sBe
             }
 }
 
-template <int D>
+// Eight consecutive elements of a q/k/v row as one bf16 MFMA operand: bf16
+// inputs as they are, float32 inputs rounded to nearest even.
+template <bool F32>
+__device__ __forceinline__ bf16x8 ld8_in(const void* base, size_t elem) {
+    if constexpr (F32) {
+        const float* p = static_cast<const float*>(base) + elem;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+        return as_bf16x8(u32x4{cvt2(a[0], a[1]), cvt2(a[2], a[3]), cvt2(b[0], b[1]), cvt2(b[2], b[3])});
+    } else {
+        return ld16_bf16(static_cast<const uint16_t*>(base) + elem);
+    }
+}
+
+// Float32 inputs: the chunk's V rows of head h as a bf16 image (zero past
+// the sequence end), lane -> rows 16 t + l%16, columns 8 (l/16) + 32 c ...
+template <class L, int D>
+__device__ __forceinline__ void store_v_image(const void* v, char* wsb, size_t t0, int nvalid, int H,
+                                              int h, int lane) {
+    const int lr = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + lr;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            const int d0 = 32 * c + 8 * grp;
+            const bf16x8 x = r < nvalid ? ld8_in<true>(v, ((t0 + r) * H + h) * D + d0) : zero_bf16x8();
+            *reinterpret_cast<bf16x8*>(wsb + L::kVI + (static_cast<size_t>(r) * D + d0) * 2) = x;
+        }
+    }
+}
+
+template <int D, bool F32>
 __global__ void __launch_bounds__(64)
-prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                    const float* __restrict__ g, const float* __restrict__ beta,
-                    char* __restrict__ ws, SeqGeom geo, int H, int Hqk, int group, bool tiled) {
-    using L = Ws<D>;
+prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
+                    const void* __restrict__ v, const float* __restrict__ g,
+                    const float* __restrict__ beta, char* __restrict__ ws, SeqGeom geo, int H,
+                    int Hqk, int group, bool tiled) {
+    using L = WsL<D, false, F32>;
     constexpr int KS = L::KS;
     // A (fp32) during the solve, then the hi/lo transpose of T1 (bf16); a
     // barrier separates the two uses.
@@ -416,8 +468,8 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     // fragments of the chunk's q and k rows (zero beyond the sequence end)
-    auto row_ptr = [&](const uint16_t* base, int r) {  // q or k row t0 + r
-        return base + ((static_cast<size_t>(t0) + r) * Hqk + hq) * D;
+    auto row_at = [&](int r) {  // element offset of q or k row t0 + r
+        return ((static_cast<size_t>(t0) + r) * Hqk + hq) * D;
     };
     bf16x8 kf[4][KS];
 #pragma unroll
@@ -425,7 +477,16 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const int r = 16 * t + lr;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            kf[t][ks] = r < nvalid ? ld16_bf16(row_ptr(k, r) + 32 * ks + 8 * grp) : zero_bf16x8();
+            kf[t][ks] = r < nvalid ? ld8_in<F32>(k, row_at(r) + 32 * ks + 8 * grp) : zero_bf16x8();
+    }
+    if constexpr (F32) {  // the bf16 K and V images for the chain
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                *reinterpret_cast<bf16x8*>(wsb + L::kKI + (static_cast<size_t>(16 * t + lr) * D + 32 * ks + 8 * grp) * 2) =
+                    kf[t][ks];
+        store_v_image<L, D>(v, wsb, t0, nvalid, H, h, lane);
     }
     __syncthreads();
 
@@ -455,7 +516,15 @@ prefill_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const int r = 16 * t + lr;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qp[t][ks] = r < nvalid ? ld16_bf16(row_ptr(q, r) + 32 * ks + 8 * grp) : zero_bf16x8();
+            qp[t][ks] = r < nvalid ? ld8_in<F32>(q, row_at(r) + 32 * ks + 8 * grp) : zero_bf16x8();
+    }
+    if constexpr (F32) {  // the bf16 Q image for the chain
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                *reinterpret_cast<bf16x8*>(wsb + L::kQI + (static_cast<size_t>(16 * t + lr) * D + 32 * ks + 8 * grp) * 2) =
+                    qp[t][ks];
     }
 
     // QKm = lower part (diagonal included) of exp(G_r - G_s) o (Q K^T), as
@@ -535,12 +604,13 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
     return as_bf16x8(u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])});
 }
 
-template <int D>
+template <int D, bool F32>
 __global__ void __launch_bounds__(64)
-prefill_prep_kda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                        const float* __restrict__ g, const float* __restrict__ beta,
-                        char* __restrict__ ws, SeqGeom geo, int H, int Hqk, int group, bool tiled) {
-    using L = WsKda<D>;
+prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
+                        const void* __restrict__ v, const float* __restrict__ g,
+                        const float* __restrict__ beta, char* __restrict__ ws, SeqGeom geo, int H,
+                        int Hqk, int group, bool tiled) {
+    using L = WsL<D, true, F32>;
     constexpr int KS = D / 32;
     __shared__ __attribute__((aligned(16))) float sA[kC][kC];
     __shared__ float sBeta[kC];
@@ -562,6 +632,7 @@ prefill_prep_kda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     char* wsb = ws + static_cast<size_t>(blk) * L::kBlock;
 
     sBeta[lane] = lane < nvalid ? beta[(static_cast<size_t>(t0) + lane) * H + h] : 0.f;
+    if constexpr (F32) store_v_image<L, D>(v, wsb, t0, nvalid, H, h, lane);
 
     // pair p = mt (mt + 1) / 2 + nt of row tile mt and column tile nt <= mt
     f32x4 accA[10], accQ[10];
@@ -593,8 +664,8 @@ prefill_prep_kda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                 const size_t tok = static_cast<size_t>(t0) + r;
                 const f32x4 g0 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * D + d0);
                 const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * D + d0 + 4);
-                kb[t] = *reinterpret_cast<const u32x4*>(k + (tok * Hqk + hq) * D + d0);
-                qb[t] = *reinterpret_cast<const u32x4*>(q + (tok * Hqk + hq) * D + d0);
+                kb[t] = __builtin_bit_cast(u32x4, ld8_in<F32>(k, (tok * Hqk + hq) * D + d0));
+                qb[t] = __builtin_bit_cast(u32x4, ld8_in<F32>(q, (tok * Hqk + hq) * D + d0));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     G[t][j] = g0[j];
@@ -795,14 +866,17 @@ __device__ __forceinline__ bf16x8 ld_split(const uint16_t* p0, const uint16_t* p
     return join(*reinterpret_cast<const u32x2*>(p0), *reinterpret_cast<const u32x2*>(p1));
 }
 
-template <int D, bool KDA>
+template <int D, bool KDA, bool F32>
 __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
                      float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
                      int Hqk, int group, bool tiled, int K, float* __restrict__ final_state) {
-    using L = std::conditional_t<KDA, WsKda<D>, Ws<D>>;
+    using L = WsL<D, KDA, F32>;
     using M = ChainLds<D, KDA>;
+    // K and Q come from the workspace's images for KDA and for float32
+    // inputs, V for float32 inputs; otherwise straight from the bf16 inputs
+    constexpr bool kImgKQ = KDA || F32;
     constexpr int kRing = M::kRing;
     constexpr int NCB = D / 16;        // column blocks per head
     constexpr int KS = L::KS;          // k-steps over d_k
@@ -1140,15 +1214,18 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     const int rr = p / PPR;
                     const int piece = 16 * ((p % PPR) ^ k_swz<D>(rr));
                     char* dst = slot + M::kK + im * (kC * D * 2) + 1024 * pi;
-                    if constexpr (KDA) {  // the workspace's row-major images
-                        dma16(rw, dst, (im == 0 ? L::kKG : L::kQG) + rr * (D * 2) + piece);
+                    if constexpr (kImgKQ) {  // the workspace's row-major images
+                        dma16(rw, dst, (im == 0 ? L::kKI : L::kQI) + rr * (D * 2) + piece);
                     } else {
                         dma16(im == 1 ? rq : rk, dst, rr * rowq_b16 + piece);
                     }
                 } else {
                     const int jv = i - 1 - M::kImages * KPT;
                     const int p = 64 * jv + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
-                    dma16(rv, slot + M::kV + 1024 * jv, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
+                    if constexpr (F32)
+                        dma16(rw, slot + M::kV + 1024 * jv, L::kVI + (p >> 1) * (D * 2) + (cb * 16 + 8 * (p & 1)) * 2);
+                    else
+                        dma16(rv, slot + M::kV + 1024 * jv, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
                 }
             }
         };
@@ -1203,7 +1280,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D, bool KDA>
+template <int D, bool KDA, bool F32>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     char* ws = static_cast<char*>(a.workspace);
     SeqGeom geo;
@@ -1226,27 +1303,34 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         geo.CT = a.B * geo.NC;
     }
     const dim3 prep_grid(static_cast<unsigned>(a.H) * geo.CT);
-    const auto* q = static_cast<const uint16_t*>(a.q);
-    const auto* k = static_cast<const uint16_t*>(a.k);
     if (KDA)
-        hipLaunchKernelGGL(prefill_prep_kda_kernel<D>, prep_grid, dim3(64), 0, stream, q, k, a.g,
-                           a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
+        hipLaunchKernelGGL((prefill_prep_kda_kernel<D, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k,
+                           a.v, a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     else
-        hipLaunchKernelGGL(prefill_prep_kernel<D>, prep_grid, dim3(64), 0, stream, q, k, a.g, a.beta,
-                           ws, geo, a.H, a.Hqk, a.group, a.tiled);
+        hipLaunchKernelGGL((prefill_prep_kernel<D, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k, a.v,
+                           a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // with float32 inputs the chain reads only the workspace's bf16 images
+    // (the input pointers are passed but never read)
+    const auto* q = static_cast<const uint16_t*>(a.q);
+    const auto* k = static_cast<const uint16_t*>(a.k);
+    const auto* v = static_cast<const uint16_t*>(a.v);
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
-    hipLaunchKernelGGL((prefill_chain_kernel<D, KDA>), dim3(bh * (D / 16)), dim3(kChainThreads), 0,
-                       stream, q, k, static_cast<const uint16_t*>(a.v), a.state, a.o, ws, geo, a.H,
-                       a.Hqk, a.group, a.tiled, a.K, a.final_state);
+    hipLaunchKernelGGL((prefill_chain_kernel<D, KDA, F32>), dim3(bh * (D / 16)), dim3(kChainThreads), 0,
+                       stream, q, k, v, a.state, a.o, ws, geo, a.H, a.Hqk, a.group, a.tiled, a.K,
+                       a.final_state);
     return hipGetLastError();
 }
 
+template <bool KDA, bool F32>
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
+    return a.d == 128 ? launch_prefill_t<128, KDA, F32>(a, stream) : launch_prefill_t<64, KDA, F32>(a, stream);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-    if (a.kda)
-        return a.d == 128 ? launch_prefill_t<128, true>(a, stream) : launch_prefill_t<64, true>(a, stream);
-    return a.d == 128 ? launch_prefill_t<128, false>(a, stream) : launch_prefill_t<64, false>(a, stream);
+    if (a.kda) return a.f32 ? launch_prefill_d<true, true>(a, stream) : launch_prefill_d<true, false>(a, stream);
+    return a.f32 ? launch_prefill_d<false, true>(a, stream) : launch_prefill_d<false, false>(a, stream);
 }
 
 }  // namespace gdn

@@ -202,3 +202,20 @@ def test_prefill_kda_validation(lib):
               None) == ERR_UNSUP
     assert pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
     assert pk(1, 0, 4, 4, 0, 128, 128, 64, N, N, N, N, N, P, N, N, 0, None) == OK
+
+
+def test_prefill_ex_validation(lib):
+    wsz = lib.gdn_prefill_workspace_size_ex
+    gda_bf, gda_f, kda_bf, kda_f = (wsz(1, 100, 4, 128, 128, 64, dt, gt) for dt, gt in
+                                    ((1, 0), (0, 0), (1, 1), (0, 1)))
+    assert 0 < gda_bf < gda_f and gda_bf < kda_bf < kda_f  # images for f32 inputs and for KDA
+    assert gda_bf == lib.gdn_prefill_workspace_size(1, 100, 4, 128, 128, 64)
+    assert wsz(1, 100, 4, 128, 128, 64, 2, 0) == 0 and wsz(1, 100, 4, 128, 128, 64, 1, 2) == 0
+    pe = lib.gdn_prefill_chunked_ex
+    # B, T, H, H_qk, map, dk, dv, chunk, dtype, gate, K, q, k, v, g, beta, state, final, o, ws, ws_bytes, stream
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 0, P, P, P, P, P, P, N, P, P, gda_f, None) == ERR_SHAPE
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 5, 0, 1, P, P, P, P, P, P, N, P, P, gda_f, None) == ERR_UNSUP
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, P, P, N, P, P, kda_bf, None) == ERR_UNSUP
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 1, P, P, P, P, P, P, N, P, P, gda_f - 1, None) == ERR_WS
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, P, P, P, P, P, P, N, P, P, kda_f - 1, None) == ERR_WS
+    assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, P, N, N, N, 0, None) == OK
