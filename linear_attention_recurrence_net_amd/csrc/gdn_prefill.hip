@@ -843,22 +843,26 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
 // KDA: the K and Q images are the decayed images KG and QG of the
 // workspace (the state update's K^T operand goes from the workspace straight
 // to the state wavefronts' registers).
+//
+// Four slots: the loads of a chunk go out three chunks ahead of its use,
+// which covers the latency of the direct-to-LDS loads from memory; the V
+// block (four values per state lane) goes to registers instead, so that
+// four slots fit.
 template <int D, bool KDA>
 struct ChainLds {
     static constexpr int kImages = 2;
     static constexpr int kE = 0;                           // gate block (Ws<D>::kE layout)
     static constexpr int kK = kE + 1024;                   // K image (KDA: KG)
     static constexpr int kQ = kK + kC * D * 2;             // Q image (KDA: QG)
-    static constexpr int kV = kK + kImages * kC * D * 2;   // V block, [64][16] bf16
-    static constexpr int kSlot = kV + kC * 16 * 2;
-    static constexpr int kLoads = 1 + kImages * (kC * D * 2 / 1024) + 2;  // 1 KiB loads per chunk
-    static constexpr int kRing = 3;
+    static constexpr int kSlot = kK + kImages * kC * D * 2;
+    static constexpr int kLoads = 1 + kImages * (kC * D * 2 / 1024);  // 1 KiB loads per chunk
+    static constexpr int kRing = 4;
     static constexpr int kAhead = kRing - 1;  // chunks loaded ahead of the one in use
 };
 
 constexpr int kStateWaves = 4;   // chunk rows 16 w.., state rows (d_k / 4) w..
 constexpr int kOutWaves = 4;     // chunk rows 16 w.. of the output
-constexpr int kLoadWaves = 2;
+constexpr int kLoadWaves = 4;
 constexpr int kChainThreads = 64 * (kStateWaves + kOutWaves + kLoadWaves + 1);  // + the storer
 
 // Two 8-byte LDS reads -> one split-order operand (k = c + 0..3 and c + 16 + 0..3).
@@ -957,6 +961,29 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     t1[ks][hl] = as_bf16x8(buf_ld16(rw, L::kT1F + frag_off(w, ks, hl, lane)));
         };
         load_t1(0);
+        // V at this lane's rows 16 w + 4 grp + j (j = 0..3) and column `col`
+        // of a chunk, bf16 bits in the low half (zero past the sequence end)
+        uint32_t vr[4];
+        auto load_v = [&](int n) {
+            const int r0 = n * kC;
+            __amdgpu_buffer_rsrc_t rv;
+            int rowb, off0;
+            if constexpr (F32) {  // the workspace's bf16 V image
+                rv = ws_rsrc(n);
+                rowb = D * 2;
+                off0 = L::kVI + col * 2;
+            } else {
+                const int row_b16 = H * D * 2;
+                rv = make_rsrc(v + (static_cast<size_t>(start + r0) * H + h) * D,
+                               (len - 1 - r0) * row_b16 + D * 2);
+                rowb = row_b16;
+                off0 = col * 2;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                vr[j] = __builtin_amdgcn_raw_buffer_load_b16(rv, off0 + (16 * w + 4 * grp + j) * rowb, 0, 0);
+        };
+        load_v(0);
         bf16x8 kt[SMT][2];
         // KDA: the state update's K^T operands, in fragment order in the workspace
         auto load_kt = [&](int n) {
@@ -974,7 +1001,6 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int n = 0; n < NC; ++n) {
             const char* slot = sL[n % kRing];
             const uint16_t* sK = reinterpret_cast<const uint16_t*>(slot + M::kK);
-            const uint16_t* sV = reinterpret_cast<const uint16_t*>(slot + M::kV);
             const float* E = reinterpret_cast<const float*>(slot + M::kE);
             lds_barrier();  // B1: chunk n's operands and start state are in LDS
 
@@ -1001,16 +1027,15 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 er = *reinterpret_cast<const f32x4*>(&E[kEr + 16 * w + 4 * grp]);
                 el = E[kEl];
             }
-            const u32x2 vv = ld_tr(&sV[(16 * w + 4 * grp + (lr >> 2)) * 16 + 4 * (lr & 3)]);
 
             // R = V - exp(G) X (KDA: V - X, the decay is inside KG) for this
             // wavefront's rows, hi/lo to LDS
             {
                 u32x2 rh, rl;
-                split4(__uint_as_float(vv[0] << 16) - eg[0] * X[0],
-                       __uint_as_float(vv[0] & 0xffff0000u) - eg[1] * X[1],
-                       __uint_as_float(vv[1] << 16) - eg[2] * X[2],
-                       __uint_as_float(vv[1] & 0xffff0000u) - eg[3] * X[3], rh, rl);
+                split4(__uint_as_float(vr[0] << 16) - eg[0] * X[0],
+                       __uint_as_float(vr[1] << 16) - eg[1] * X[1],
+                       __uint_as_float(vr[2] << 16) - eg[2] * X[2],
+                       __uint_as_float(vr[3] << 16) - eg[3] * X[3], rh, rl);
                 *reinterpret_cast<u32x2*>(&sR[0][lr][16 * w + 4 * grp]) = rh;
                 *reinterpret_cast<u32x2*>(&sR[1][lr][16 * w + 4 * grp]) = rl;
             }
@@ -1028,6 +1053,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 W = mfma(t1[ks][1], rh, W);
             }
             load_t1(min(n + 1, NC - 1));  // t1 is not read again in this chunk
+            load_v(min(n + 1, NC - 1));   // nor vr
             // K^T operands of the state update (d_k rows SRW w + 16 mt + l%16,
             // chunk rows in split order), read while W forms (KDA: loaded
             // during the previous chunk)
@@ -1176,20 +1202,20 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // Each loader issues the same number of 1 KiB direct-to-LDS loads per
         // chunk (kPer, the last one repeated where the count does not
         // divide), in three parts, one after each barrier.  The loads of
-        // chunk n + kAhead (= 2) go out during chunk n, and before chunk
+        // chunk n + kAhead (= 3) go out during chunk n, and before chunk
         // n + 1's first barrier each loader waits until chunk n + 1's loads are
-        // done: only its kPer newest loads, those of chunk n + 2, may stay
-        // outstanding.
+        // done: only its 2 kPer newest loads, those of chunks n + 2 and n + 3,
+        // may stay outstanding.  Slot (n + 3) % 4 held chunk n - 1, whose last
+        // reads come before chunk n's first barrier.
         const int l = wave - kStateWaves - kOutWaves;
         const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
-        const size_t head0 = (static_cast<size_t>(start) * H + h) * D;      // v element (start, h, 0)
         const size_t headq0 = (static_cast<size_t>(start) * Hqk + hq) * D;  // q/k element (start, hq, 0)
-        const int row_b16 = H * D * 2;                                      // bytes per token of v
         const int rowq_b16 = Hqk * D * 2;                                   // bytes per token of q, k
-        const int seq_b16 = (len - 1) * row_b16 + D * 2;    // end of the last valid row of v
-        const int seqq_b16 = (len - 1) * rowq_b16 + D * 2;  // and of q, k
+        const int seqq_b16 = (len - 1) * rowq_b16 + D * 2;  // end of the last valid row of q, k
         constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
-        constexpr int kPart = (kPer + 2) / 3;
+        // parts of kP01, kP01 and the rest: little is left for after B3, so
+        // that a loader reaches B1 (after waiting for the next chunk) early
+        constexpr int kP01 = kPer / 2;
         auto load = [&](int n, int qt) {
             char* slot = sL[n % kRing];
             const int r0 = n * kC;
@@ -1198,16 +1224,14 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 make_rsrc(k + headq0 + static_cast<size_t>(r0) * Hqk * D, seqq_b16 - r0 * rowq_b16);
             const __amdgpu_buffer_rsrc_t rq =
                 make_rsrc(q + headq0 + static_cast<size_t>(r0) * Hqk * D, seqq_b16 - r0 * rowq_b16);
-            const __amdgpu_buffer_rsrc_t rv =
-                make_rsrc(v + head0 + static_cast<size_t>(r0) * H * D, seq_b16 - r0 * row_b16);
+            const int j0 = qt * kP01, j1 = qt == 2 ? kPer : (qt + 1) * kP01;
 #pragma unroll
-            for (int jj = 0; jj < kPart; ++jj) {
-                const int j = kPart * qt + jj;
-                if (j >= kPer) break;
+            for (int j = 0; j < kPer; ++j) {
+                if (j < j0 || j >= j1) continue;
                 const int i = min(kPer * l + j, M::kLoads - 1);
                 if (i == 0) {
                     dma16(rw, slot + M::kE, L::kE + 16 * lane);
-                } else if (i < 1 + M::kImages * KPT) {
+                } else {
                     const int im = (i - 1) / KPT;  // image: K (KG), then Q (QG)
                     const int pi = i - 1 - im * KPT;
                     const int p = 64 * pi + lane;  // image piece: row p / PPR, slot p % PPR
@@ -1219,13 +1243,6 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     } else {
                         dma16(im == 1 ? rq : rk, dst, rr * rowq_b16 + piece);
                     }
-                } else {
-                    const int jv = i - 1 - M::kImages * KPT;
-                    const int p = 64 * jv + lane;  // row p / 2, columns 8 (p % 2) + 0..7 of the block
-                    if constexpr (F32)
-                        dma16(rw, slot + M::kV + 1024 * jv, L::kVI + (p >> 1) * (D * 2) + (cb * 16 + 8 * (p & 1)) * 2);
-                    else
-                        dma16(rv, slot + M::kV + 1024 * jv, (p >> 1) * row_b16 + (cb * 16 + 8 * (p & 1)) * 2);
                 }
             }
         };
@@ -1243,8 +1260,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             lds_barrier();  // B3
             if (more) {
                 load(n + A, 2);
-                if constexpr (A == 2) vm_wait_keep<kPer>();  // chunk n + 1's loads are done
-                else vm_wait_all();
+                vm_wait_keep<(A - 1) * kPer>();  // chunk n + 1's loads are done
             } else {
                 vm_wait_all();
             }
@@ -1257,9 +1273,9 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // chunk n's output block from sO to o: lane -> row lane / 4 + 16 i,
         // columns 4 (lane % 4) + 0..3 of the block, read as two 8-byte halves
         float* const obase = o + (static_cast<size_t>(start) * H + h) * D + cb * 16 + 4 * (lane & 3);
-        auto store_o = [&](int n) {
+        auto store_o = [&](int n, int i0) {  // rows 16 i + lane / 4, i = i0, i0 + 1
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = i0; i < i0 + 2; ++i) {
                 const int rr = 16 * i + (lane >> 2);
                 const float* src = &sO[rr][4 * (lane & 3)];
                 const f32x2 a = *reinterpret_cast<const f32x2*>(src);
@@ -1269,14 +1285,17 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * D) = f32x4{a[0], a[1], c[0], c[1]};
             }
         };
+        // half of the block after B1, half after B2: sO is rewritten after B3
         for (int n = 0; n < NC; ++n) {
             lds_barrier();  // B1: chunk n - 1's output is in sO
-            if (n > 0) store_o(n - 1);
+            if (n > 0) store_o(n - 1, 0);
             lds_barrier();  // B2
+            if (n > 0) store_o(n - 1, 2);
             lds_barrier();  // B3
         }
         lds_barrier();  // final barrier
-        store_o(NC - 1);
+        store_o(NC - 1, 0);
+        store_o(NC - 1, 2);
     }
 }
 
