@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "684eea692babf06e36dab55bb06d90a7a541af8d246c790b81ee4a3753886dc9",
-    "fetch_kib": 33508.5,       # median over 62 decode dispatches
-    "write_kib": 66079.5,
+    "sha256": "2ea2dcb101547c08ab1d7690d4f9b89a1800f8639b77a7ede0fdb53449037a7e",
+    "fetch_kib": 33508.59375,       # median over 62 decode dispatches
+    "write_kib": 66080.75,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }

@@ -4,6 +4,7 @@
 
 #include "gdn.h"
 #include "gdn_internal.hpp"
+#include "gdn_prefill_args.hpp"
 
 namespace {
 

@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "gdn_internal.hpp"
+#include "gdn_prefill_args.hpp"
 
 namespace gdn {
 
