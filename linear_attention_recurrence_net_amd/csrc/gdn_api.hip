@@ -10,7 +10,10 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool supported_head(int d_k, int d_v) { return d_k == d_v && (d_k == 64 || d_k == 128); }
+bool head_size(int d) { return d == 64 || d == 128; }
+// The token kernels take any pairing of the two head sizes.
+bool supported_head(int d_k, int d_v) { return head_size(d_k) && head_size(d_v); }
+bool supported_prefill(int d_k, int d_v) { return head_size(d_k) && d_k == d_v; }
 
 int check_launch(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
@@ -69,7 +72,8 @@ int gdn_forward_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk, int3
     a.T = T;
     a.H = H;
     a.K = K;
-    a.d = d_k;
+    a.dk = d_k;
+    a.dv = d_v;
     a.Hqk = H_qk;
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;
@@ -108,13 +112,13 @@ int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_
 
 size_t gdn_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                   int32_t chunk) {
-    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_prefill(d_k, d_v)) return 0;
     return gdn::prefill_workspace_bytes(B, T, H, d_k);
 }
 
 size_t gdn_prefill_workspace_size_ex(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                      int32_t chunk, int32_t qkv_dtype, int32_t gate) {
-    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_prefill(d_k, d_v)) return 0;
     if ((qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) || (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY))
         return 0;
     return gdn::prefill_workspace_bytes(B, T, H, d_k, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
@@ -131,7 +135,7 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
     const bool tokens = B > 0 && H > 0 && T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
-    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 64 || !supported_prefill(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
     // KDA snapshots would need every token's per-row decay inside the chain
@@ -203,7 +207,7 @@ int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_
 
 size_t gdn_prefill_varlen_workspace_size(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
                                          int32_t d_v, int32_t chunk) {
-    if (N < 0 || total_T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    if (N < 0 || total_T < 0 || H < 0 || chunk != 64 || !supported_prefill(d_k, d_v)) return 0;
     return gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k);
 }
 
@@ -219,7 +223,7 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     const bool tokens = N > 0 && H > 0 && total_T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (N > 0 && H > 0 && !state) return GDN_ERR_NULL;
-    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 64 || !supported_prefill(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
         return GDN_ERR_UNSUPPORTED;
     if (N == 0 || H == 0 || total_T == 0) return GDN_OK;

@@ -20,10 +20,11 @@ struct RecurrentArgs {
     const void* v;
     const float* g;
     const float* beta;
-    float* state;        // [B,H,K,d,d]
-    float* final_state;  // [B,H,d,d] or nullptr
-    float* o;            // [B,T,H,d]
-    int B, T, H, K, d;
+    float* state;        // [B,H,K,dk,dv]
+    float* final_state;  // [B,H,dk,dv] or nullptr
+    float* o;            // [B,T,H,dv]
+    int B, T, H, K;
+    int dk, dv;          // key and value head sizes, each 64 or 128
     int Hqk;             // q/k heads: value head h reads q/k head qk_head(h)
     int group;           // H / Hqk
     bool tiled;          // qk_head(h) = tiled ? h % Hqk : h / group

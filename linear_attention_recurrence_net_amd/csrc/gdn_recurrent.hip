@@ -90,10 +90,10 @@ struct TokenRaw {
     // (sequence, token, q/k head) of q and k.
     __device__ __forceinline__ void load(const void* q, const void* k, const void* v,
                                          const float* gp, const float* bp, size_t bth,
-                                         size_t bthq, int row0, int col0, int D) {
+                                         size_t bthq, int row0, int col0, int DK, int DV) {
         static_assert(KW % 2 == 0, "row slices are loaded 64 or 128 bits at a time");
-        const size_t ko = bthq * D + row0;
-        const size_t vo = bth * D + col0;
+        const size_t ko = bthq * DK + row0;  // key index row0 of q and k
+        const size_t vo = bth * DV + col0;   // value index col0 of v
         const uint32_t* kp = reinterpret_cast<const uint32_t*>(
             static_cast<const char*>(k) + ko * (BF16 ? 2 : 4));
         const uint32_t* qp = reinterpret_cast<const uint32_t*>(
@@ -124,7 +124,7 @@ struct TokenRaw {
         }
         if constexpr (KDA) {
             float tmp[RPL];
-            load_vec<RPL, false>(gp, bth * D + row0, tmp);
+            load_vec<RPL, false>(gp, bth * DK + row0, tmp);
 #pragma unroll
             for (int i = 0; i < RPL; ++i) g[i] = tmp[i];
         } else {
@@ -165,9 +165,10 @@ struct TokenRaw {
 }  // namespace
 
 // ONE: the launch has exactly one token and no snapshot (plain decode); the
-// token loop is then straight-line code.
-template <int D, bool KDA, bool BF16, bool ONE>
-__global__ void __launch_bounds__(waves_per_group<D>() * kWave)
+// token loop is then straight-line code.  DK and DV: key and value head
+// sizes (state rows and columns).
+template <int DK, int DV, bool KDA, bool BF16, bool ONE>
+__global__ void __launch_bounds__(waves_per_group<DV>() * kWave)
 #if GDN_DEC_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(GDN_DEC_WAVES_PER_EU)))
 #endif
@@ -178,11 +179,11 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  int n_snap, int Hqk, int group, bool tiled) {
     constexpr int CG = kCPW / 4;     // lanes across one row segment
     constexpr int RG = kWave / CG;   // row groups
-    constexpr int RPL = D / RG;      // rows held per lane
-    constexpr int WPG = waves_per_group<D>();
-    constexpr int NB = D / (kCPW * WPG);  // workgroups per head
-    constexpr size_t TILE = static_cast<size_t>(D) * D;
-    static_assert(RPL >= 1 && D % (kCPW * WPG) == 0, "tiling");
+    constexpr int RPL = DK / RG;     // rows held per lane
+    constexpr int WPG = waves_per_group<DV>();
+    constexpr int NB = DV / (kCPW * WPG);  // workgroups per head
+    constexpr size_t TILE = static_cast<size_t>(DK) * DV;
+    static_assert(RPL >= 1 && DK % RG == 0 && DV % (kCPW * WPG) == 0, "tiling");
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
@@ -200,7 +201,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
 
     f32x4 s[RPL];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) s[i] = load_state(slots + static_cast<size_t>(row0 + i) * D + col0);
+    for (int i = 0; i < RPL; ++i) s[i] = load_state(slots + static_cast<size_t>(row0 + i) * DV + col0);
 
     // Raw inputs of one token, as loaded (bf16 stays packed until used).
     using Raw = TokenRaw<RPL, KDA, BF16>;
@@ -208,14 +209,14 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     Raw cur;
     if (n_tok > 0)
         cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h,
-                 (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, D);
+                 (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, DK, DV);
 
     for (int t = 0; t < n_tok; ++t) {
         const size_t bth = (static_cast<size_t>(b) * T + t) * H + h;
         const size_t bthq = (static_cast<size_t>(b) * T + t) * Hqk + hq;
         // prefetch the next token while this one is computed
         Raw nxt;
-        if (!ONE && t + 1 < n_tok) nxt.load(q, k, v, g, beta, bth + H, bthq + Hqk, row0, col0, D);
+        if (!ONE && t + 1 < n_tok) nxt.load(q, k, v, g, beta, bth + H, bthq + Hqk, row0, col0, DK, DV);
 
         float kv[RPL], qv[RPL];
         cur.unpack_kq(kv, qv);
@@ -272,7 +273,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         const float w3 = bt * (vv.w - u3);
 
         if (rg == 0) {
-            st4(o + bth * D + col0,
+            st4(o + bth * DV + col0,
                 f32x4{fmaf(kq, w0, p0), fmaf(kq, w1, p1), fmaf(kq, w2, p2), fmaf(kq, w3, p3)});
         }
 
@@ -289,47 +290,50 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         if (!ONE && t < n_snap) {
             float* dst = slots + static_cast<size_t>(t + 1) * TILE;
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * D + col0, s[i]);
+            for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * DV + col0, s[i]);
         }
         if (!ONE) cur = nxt;
     }
 
     if (K == 1) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) store_state(slots + static_cast<size_t>(row0 + i) * D + col0, s[i]);
+        for (int i = 0; i < RPL; ++i) store_state(slots + static_cast<size_t>(row0 + i) * DV + col0, s[i]);
     }
     if (final_state != nullptr) {
         float* dst = final_state + static_cast<size_t>(bh) * TILE;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * D + col0, s[i]);
+        for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * DV + col0, s[i]);
     }
 }
 
-template <int D, bool KDA, bool BF16>
+template <int DK, int DV, bool KDA, bool BF16>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
-    constexpr int WPG = waves_per_group<D>();
-    constexpr int NB = D / (kCPW * WPG);
+    constexpr int WPG = waves_per_group<DV>();
+    constexpr int NB = DV / (kCPW * WPG);
     dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * NB);
     dim3 block(WPG * kWave);
     if (a.T == 1 && a.n_snap == 0)
-        hipLaunchKernelGGL((recurrent_kernel<D, KDA, BF16, true>), grid, block, 0, stream, a.q,
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, true>), grid, block, 0, stream, a.q,
                            a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
                            a.n_snap, a.Hqk, a.group, a.tiled);
     else
-        hipLaunchKernelGGL((recurrent_kernel<D, KDA, BF16, false>), grid, block, 0, stream, a.q,
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, false>), grid, block, 0, stream, a.q,
                            a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
                            a.n_snap, a.Hqk, a.group, a.tiled);
     return hipGetLastError();
 }
 
+template <int DK, int DV>
+static hipError_t launch_recurrent_d(const RecurrentArgs& a, hipStream_t stream) {
+    if (a.kda)
+        return a.bf16 ? launch_recurrent_t<DK, DV, true, true>(a, stream) : launch_recurrent_t<DK, DV, true, false>(a, stream);
+    return a.bf16 ? launch_recurrent_t<DK, DV, false, true>(a, stream) : launch_recurrent_t<DK, DV, false, false>(a, stream);
+}
+
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
-    const bool bf = a.bf16, kda = a.kda;
-    if (a.d == 128) {
-        if (kda) return bf ? launch_recurrent_t<128, true, true>(a, stream) : launch_recurrent_t<128, true, false>(a, stream);
-        return bf ? launch_recurrent_t<128, false, true>(a, stream) : launch_recurrent_t<128, false, false>(a, stream);
-    }
-    if (kda) return bf ? launch_recurrent_t<64, true, true>(a, stream) : launch_recurrent_t<64, true, false>(a, stream);
-    return bf ? launch_recurrent_t<64, false, true>(a, stream) : launch_recurrent_t<64, false, false>(a, stream);
+    if (a.dk == 128)
+        return a.dv == 128 ? launch_recurrent_d<128, 128>(a, stream) : launch_recurrent_d<128, 64>(a, stream);
+    return a.dv == 128 ? launch_recurrent_d<64, 128>(a, stream) : launch_recurrent_d<64, 64>(a, stream);
 }
 
 }  // namespace gdn

@@ -30,8 +30,8 @@ import gdn_inputs as gi
 import oracle
 
 
-def _rand_case(B, T, H, d, K=1, gate="gda", seed=0, zero_state=False):
-    c = gi.make_case(B, T, H, d, K=K, gate=gate, qkv_dtype="f32", seed=seed,
+def _rand_case(B, T, H, d, K=1, gate="gda", seed=0, zero_state=False, d_v=None):
+    c = gi.make_case(B, T, H, d, d_v, K=K, gate=gate, qkv_dtype="f32", seed=seed,
                      zero_state=zero_state)
     return (c.f64("q"), c.f64("k"), c.f64("v"), c.f64("g"), c.f64("beta"),
             c.f64("state"))
@@ -130,6 +130,38 @@ def test_two_token_brute_force_product_form(kda):
                 S = P @ D @ S + beta[b, t, h] * kt @ v[b, t, h][None, :]
                 np.testing.assert_allclose(o[b, t, h], S.T @ q[b, t, h], rtol=1e-12, atol=1e-14)
             np.testing.assert_allclose(st_out[b, h, 0], S, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("dk,dv", [(6, 10), (10, 6)])
+def test_two_token_brute_force_unequal_head_sizes(kda, dk, dv):
+    """The same product form with a d_k x d_v state, d_k != d_v (q, k, the
+    gates and the state rows on the key axis; v, o and the columns on the
+    value axis)."""
+    q, k, v, g, beta, st = _rand_case(2, 2, 3, dk, gate="kda" if kda else "gda", seed=13, d_v=dv)
+    assert st.shape[-2:] == (dk, dv) and v.shape[-1] == dv
+    o, st_out, _ = oracle.forward(q, k, v, g, beta, st, kda=kda)
+    assert o.shape[-1] == dv
+    B, T, H, _ = q.shape
+    for b in range(B):
+        for h in range(H):
+            S = st[b, h, 0].copy()
+            for t in range(T):
+                kt = k[b, t, h][:, None]
+                D = np.diag(np.exp(g[b, t, h])) if kda else math.exp(g[b, t, h]) * np.eye(dk)
+                P = np.eye(dk) - beta[b, t, h] * (kt @ kt.T)
+                S = P @ D @ S + beta[b, t, h] * kt @ v[b, t, h][None, :]
+                np.testing.assert_allclose(o[b, t, h], S.T @ q[b, t, h], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(st_out[b, h, 0], S, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_chunked_equals_sequential_unequal_head_sizes(kda):
+    q, k, v, g, beta, st = _rand_case(1, 90, 2, 16, gate="kda" if kda else "gda", seed=29, d_v=24)
+    o, s, _ = oracle.forward(q, k, v, g, beta, st, kda=kda)
+    oc, sc = oracle.chunked(q, k, v, g, beta, st[:, :, 0], chunk=32, kda=kda)
+    assert np.abs(oc - o).max() <= 1e-10 * np.abs(o).max()
+    assert np.abs(sc - s[:, :, 0]).max() <= 1e-10 * np.abs(s).max()
 
 
 # ---------------------------------------------------------------- invariants 3, 4
