@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "2ea2dcb101547c08ab1d7690d4f9b89a1800f8639b77a7ede0fdb53449037a7e",
+    "sha256": "3144bf48ee78d74c90ecdd8e155bd5aa5d5e406c39942e9a646ae4a7474f67ae",
     "fetch_kib": 33508.59375,       # median over 62 decode dispatches
-    "write_kib": 66080.75,
+    "write_kib": 66079.125,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
@@ -642,7 +642,7 @@ def main():
             "unit": "GB/s",
             "frac": dec["achieved_gbs"] / HBM_PEAK_GBS,
             "traffic": decode_traffic_bytes(),
-            "kernel": "gdn::recurrent_kernel<128, GDA, bf16, single token>",
+            "kernel": "gdn::recurrent_kernel<d_k=128, d_v=128, GDA, bf16, single token>",
             "bytes_per_launch": dec["bytes"],
             "us_per_launch": dec["us_per_launch"],
             "eager_us_per_launch": dec["eager_us_per_launch"],

@@ -24,8 +24,9 @@
  *    [B,T,H,d_k] (KDA); beta [B,T,H]; state [B,H,K,d_k,d_v] (slot 0 = input).
  *    q/k/v are float32 or bfloat16 (qkv_dtype); g, beta, state and o are
  *    float32.  g holds LOG-gates (the decay is exp(g)).
- *  - Head sizes d_k = d_v in {64, 128} (the sizes the pages' fused kernels
- *    support; other sizes are reported as unsupported, never computed).
+ *  - Head sizes d_k and d_v each 64 or 128, in any pairing (the sizes the
+ *    pages' fused kernels support; other sizes are reported as unsupported,
+ *    never computed).
  *  - Empty problems (B, H or T equal to 0) are valid; the pointers of empty
  *    arrays may then be NULL.
  *  - All validation happens on the host before any launch.  On an error
@@ -49,7 +50,7 @@ typedef enum {
     GDN_ERR_NULL = 1,        /* a required pointer is NULL                      */
     GDN_ERR_SHAPE = 2,       /* a size is negative, K < 1, chunk < 1, or H_qk
                                 does not divide H                               */
-    GDN_ERR_UNSUPPORTED = 3, /* d_k != d_v, d not in {64,128}, bad dtype/gate   */
+    GDN_ERR_UNSUPPORTED = 3, /* d_k or d_v not in {64,128}, bad dtype/gate     */
     GDN_ERR_WORKSPACE = 4,   /* prefill workspace missing or too small          */
     GDN_ERR_HIP = 5          /* the HIP runtime reported a launch error         */
 } gdn_status;
@@ -105,8 +106,8 @@ int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_
  * Chunked prefill (llama.cpp commit log, tag b9752, bullet "llama : enable
  * chunked fused GDN path"; the chunk algebra is the WY/UT form of the same
  * recurrence and gives the same result up to rounding).
- * GDA only, q/k/v bfloat16, d_k = d_v in {64,128}, chunk = 64, any T >= 0
- * with T*H*d_k*4 < 2^31 bytes per sequence (a short final chunk behaves as if
+ * GDA only, q/k/v bfloat16, d_k and d_v in {64,128}, chunk = 64, any T >= 0
+ * with T*H*max(d_k,d_v)*4 < 2^31 bytes per sequence (a short final chunk behaves as if
  * padded with beta = 0, g = 0, k = q = v = 0).
  * state [B,H,d_k,d_v] float32 holds S_0 on entry and S_T on return;
  * o [B,T,H,d_v] float32.  Contractions run on bf16 MFMA with float32

@@ -11,9 +11,8 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool head_size(int d) { return d == 64 || d == 128; }
-// The token kernels take any pairing of the two head sizes.
+// Every kernel takes any pairing of the two head sizes.
 bool supported_head(int d_k, int d_v) { return head_size(d_k) && head_size(d_v); }
-bool supported_prefill(int d_k, int d_v) { return head_size(d_k) && d_k == d_v; }
 
 int check_launch(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
@@ -112,16 +111,16 @@ int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_
 
 size_t gdn_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                   int32_t chunk) {
-    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_prefill(d_k, d_v)) return 0;
-    return gdn::prefill_workspace_bytes(B, T, H, d_k);
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    return gdn::prefill_workspace_bytes(B, T, H, d_k, d_v);
 }
 
 size_t gdn_prefill_workspace_size_ex(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                      int32_t chunk, int32_t qkv_dtype, int32_t gate) {
-    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_prefill(d_k, d_v)) return 0;
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
     if ((qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) || (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY))
         return 0;
-    return gdn::prefill_workspace_bytes(B, T, H, d_k, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
+    return gdn::prefill_workspace_bytes(B, T, H, d_k, d_v, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
 }
 
 int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
@@ -135,7 +134,7 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
     const bool tokens = B > 0 && H > 0 && T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (B > 0 && H > 0 && !state) return GDN_ERR_NULL;
-    if (chunk != 64 || !supported_prefill(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
     // KDA snapshots would need every token's per-row decay inside the chain
@@ -154,9 +153,10 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
                                         final_state, nullptr, stream);
     }
     // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
-    if (static_cast<int64_t>(T) * H * d_k * 4 >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(T) * H * (d_k > d_v ? d_k : d_v) * 4 >= (int64_t(1) << 31))
+        return GDN_ERR_UNSUPPORTED;
     const bool kda = gate == GDN_GATE_KEY, f32 = qkv_dtype == GDN_F32;
-    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, kda, f32);
+    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, d_v, kda, f32);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_WORKSPACE;
@@ -174,7 +174,8 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
     a.B = B;
     a.T = T;
     a.H = H;
-    a.d = d_k;
+    a.dk = d_k;
+    a.dv = d_v;
     a.Hqk = H_qk;
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;
@@ -207,8 +208,8 @@ int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_
 
 size_t gdn_prefill_varlen_workspace_size(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
                                          int32_t d_v, int32_t chunk) {
-    if (N < 0 || total_T < 0 || H < 0 || chunk != 64 || !supported_prefill(d_k, d_v)) return 0;
-    return gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k);
+    if (N < 0 || total_T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
+    return gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v);
 }
 
 int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_qk,
@@ -223,13 +224,14 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     const bool tokens = N > 0 && H > 0 && total_T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (N > 0 && H > 0 && !state) return GDN_ERR_NULL;
-    if (chunk != 64 || !supported_prefill(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
         return GDN_ERR_UNSUPPORTED;
     if (N == 0 || H == 0 || total_T == 0) return GDN_OK;
     // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
-    if (static_cast<int64_t>(total_T) * H * d_k * 4 >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
-    const size_t need = gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k);
+    if (static_cast<int64_t>(total_T) * H * (d_k > d_v ? d_k : d_v) * 4 >= (int64_t(1) << 31))
+        return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_WORKSPACE;
@@ -250,7 +252,8 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     a.B = N;
     a.T = total_T;
     a.H = H;
-    a.d = d_k;
+    a.dk = d_k;
+    a.dv = d_v;
     a.Hqk = H_qk;
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;

@@ -63,9 +63,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 //   QKF  the decay-masked Q K^T as A operands, same shape and order as T1F
 //   E    fp32 [64] exp(G_r), [64] exp(G_last - G_r), [1] exp(G_last) at float 128;
 //        1 KiB in all
-template <int D>
+template <int DK>
 struct Ws {
-    static constexpr int KS = D / 32;  // MFMA k-steps over d_k
+    static constexpr int KS = DK / 32;  // MFMA k-steps over d_k
     static constexpr int kT1F = 0;
     static constexpr int kQKF = kT1F + 4 * 2 * 2 * 64 * 16;
     static constexpr int kE = kQKF + 4 * 2 * 2 * 64 * 16;
@@ -75,38 +75,40 @@ struct Ws {
 // KDA (one log-gate per key row): the same T1F, QKF and gate block, then
 // the decayed operands the chain reads in place of K and Q (rows past the end
 // of the sequence are zero):
-//   KG   K o exp(G), row-major [64][D] bf16 (row r, key i: k_r[i] exp(G_r[i]))
+//   KG   K o exp(G), row-major [64][DK] bf16 (row r, key i: k_r[i] exp(G_r[i]))
 //   QG   Q o exp(G), the same layout
 //   KDF  (K o exp(G_last - G))^T as the state update's A operands: for state
 //        wavefront w, state tile mt and k-step ks (chunk rows 32 ks.., split
-//        order), 64 lanes x 16 bytes at ((w * D/64 + mt) * 2 + ks) * 1 KiB
-// and E holds fp32 exp(G_last[i]) for the D key rows.
-template <int D>
-struct WsKda : Ws<D> {
-    static constexpr int kKG = Ws<D>::kBlock;
-    static constexpr int kQG = kKG + kC * D * 2;
-    static constexpr int kKDF = kQG + kC * D * 2;
-    static constexpr int kBlock = kKDF + kC * D * 2;
+//        order), 64 lanes x 16 bytes at ((w * DK/64 + mt) * 2 + ks) * 1 KiB
+// and E holds fp32 exp(G_last[i]) for the DK key rows.
+template <int DK>
+struct WsKda : Ws<DK> {
+    static constexpr int kKG = Ws<DK>::kBlock;
+    static constexpr int kQG = kKG + kC * DK * 2;
+    static constexpr int kKDF = kQG + kC * DK * 2;
+    static constexpr int kBlock = kKDF + kC * DK * 2;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
 // Workspace block of one (sequence, head, chunk) for each gate kind and input
 // type.  With float32 q/k/v the prep also rounds the chunk's K, Q and V rows
-// to bf16 images, row-major [64][D] (zero past the sequence end), which the
+// to bf16 images, row-major [64][DK] for K and Q and [64][DV] for V (zero
+// past the sequence end), which the
 // chain reads in place of the inputs; KDA's decayed KG and QG already are
 // such images, so KDA adds only V.
-template <int D, bool KDA, bool F32>
-struct WsL : std::conditional_t<KDA, WsKda<D>, Ws<D>> {
-    using Base = std::conditional_t<KDA, WsKda<D>, Ws<D>>;
-    static constexpr int kImg = kC * D * 2;
-    static constexpr int kKI = KDA ? WsKda<D>::kKG : Base::kBlock;        // K image the chain reads
-    static constexpr int kQI = KDA ? WsKda<D>::kQG : Base::kBlock + kImg; // Q image the chain reads
-    static constexpr int kVI = Base::kBlock + (KDA ? 0 : 2 * kImg);        // V image (F32)
-    static constexpr int kBlock = F32 ? kVI + kImg : Base::kBlock;
+template <int DK, int DV, bool KDA, bool F32>
+struct WsL : std::conditional_t<KDA, WsKda<DK>, Ws<DK>> {
+    using Base = std::conditional_t<KDA, WsKda<DK>, Ws<DK>>;
+    static constexpr int kImg = kC * DK * 2;   // a K or Q image
+    static constexpr int kImgV = kC * DV * 2;  // the V image
+    static constexpr int kKI = KDA ? WsKda<DK>::kKG : Base::kBlock;        // K image the chain reads
+    static constexpr int kQI = KDA ? WsKda<DK>::kQG : Base::kBlock + kImg; // Q image the chain reads
+    static constexpr int kVI = Base::kBlock + (KDA ? 0 : 2 * kImg);         // V image (F32)
+    static constexpr int kBlock = F32 ? kVI + kImgV : Base::kBlock;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
 // float offsets inside E
 constexpr int kEg = 0, kEr = 64, kEl = 128, kEs = 192;
-constexpr int kEv = 0;  // KDA: exp(G_last[i]), i < D
+constexpr int kEv = 0;  // KDA: exp(G_last[i]), i < DK
 
 // Byte offset of A operand (row tile t, k-step ks, hi/lo hl) of lane `lane` in T1F / QKF.
 __host__ __device__ constexpr int frag_off(int t, int ks, int hl, int lane) {
@@ -249,24 +251,25 @@ struct SeqGeom {
 static size_t table_bytes(int N) { return ((static_cast<size_t>(2 * (N + 1)) * 4 + 255) / 256) * 256; }
 
 template <bool KDA, bool F32>
-static size_t block_bytes_t(int d) {
-    return d == 128 ? WsL<128, KDA, F32>::kBlock : WsL<64, KDA, F32>::kBlock;
+static size_t block_bytes_t(int dk, int dv) {
+    if (dk == 128) return dv == 128 ? WsL<128, 128, KDA, F32>::kBlock : WsL<128, 64, KDA, F32>::kBlock;
+    return dv == 128 ? WsL<64, 128, KDA, F32>::kBlock : WsL<64, 64, KDA, F32>::kBlock;
 }
-static size_t block_bytes(int d, bool kda, bool f32) {
-    if (kda) return f32 ? block_bytes_t<true, true>(d) : block_bytes_t<true, false>(d);
-    return f32 ? block_bytes_t<false, true>(d) : block_bytes_t<false, false>(d);
+static size_t block_bytes(int dk, int dv, bool kda, bool f32) {
+    if (kda) return f32 ? block_bytes_t<true, true>(dk, dv) : block_bytes_t<true, false>(dk, dv);
+    return f32 ? block_bytes_t<false, true>(dk, dv) : block_bytes_t<false, false>(dk, dv);
 }
 
-size_t prefill_workspace_bytes(int B, int T, int H, int d, bool kda, bool f32) {
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, bool kda, bool f32) {
     const size_t nc = (static_cast<size_t>(T) + kC - 1) / kC;
-    return static_cast<size_t>(B) * H * nc * block_bytes(d, kda, f32);
+    return static_cast<size_t>(B) * H * nc * block_bytes(dk, dv, kda, f32);
 }
 
 // Variable lengths: at most total / C + N chunks over all sequences (each
 // sequence adds at most one partial chunk), plus the table.
-size_t prefill_varlen_workspace_bytes(int N, int total, int H, int d) {
+size_t prefill_varlen_workspace_bytes(int N, int total, int H, int dk, int dv) {
     const size_t ct = (static_cast<size_t>(total) + kC - 1) / kC + N;
-    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(d, false, false);
+    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(dk, dv, false, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -398,7 +401,7 @@ __device__ __forceinline__ bf16x8 ld8_in(const void* base, size_t elem) {
 
 // Float32 inputs: the chunk's V rows of head h as a bf16 image (zero past
 // the sequence end), lane -> rows 16 t + l%16, columns 8 (l/16) + 32 c ...
-template <class L, int D>
+template <class L, int DV>
 __device__ __forceinline__ void store_v_image(const void* v, char* wsb, size_t t0, int nvalid, int H,
                                               int h, int lane) {
     const int lr = lane & 15, grp = lane >> 4;
@@ -406,21 +409,21 @@ __device__ __forceinline__ void store_v_image(const void* v, char* wsb, size_t t
     for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + lr;
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
+        for (int c = 0; c < DV / 32; ++c) {
             const int d0 = 32 * c + 8 * grp;
-            const bf16x8 x = r < nvalid ? ld8_in<true>(v, ((t0 + r) * H + h) * D + d0) : zero_bf16x8();
-            *reinterpret_cast<bf16x8*>(wsb + L::kVI + (static_cast<size_t>(r) * D + d0) * 2) = x;
+            const bf16x8 x = r < nvalid ? ld8_in<true>(v, ((t0 + r) * H + h) * DV + d0) : zero_bf16x8();
+            *reinterpret_cast<bf16x8*>(wsb + L::kVI + (static_cast<size_t>(r) * DV + d0) * 2) = x;
         }
     }
 }
 
-template <int D, bool F32>
+template <int DK, int DV, bool F32>
 __global__ void __launch_bounds__(64)
 prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     const void* __restrict__ v, const float* __restrict__ g,
                     const float* __restrict__ beta, char* __restrict__ ws, SeqGeom geo, int H,
                     int Hqk, int group, bool tiled) {
-    using L = WsL<D, false, F32>;
+    using L = WsL<DK, DV, false, F32>;
     constexpr int KS = L::KS;
     // A (fp32) during the solve, then the hi/lo transpose of T1 (bf16); a
     // barrier separates the two uses.
@@ -470,7 +473,7 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
 
     // fragments of the chunk's q and k rows (zero beyond the sequence end)
     auto row_at = [&](int r) {  // element offset of q or k row t0 + r
-        return ((static_cast<size_t>(t0) + r) * Hqk + hq) * D;
+        return ((static_cast<size_t>(t0) + r) * Hqk + hq) * DK;
     };
     bf16x8 kf[4][KS];
 #pragma unroll
@@ -485,9 +488,9 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                *reinterpret_cast<bf16x8*>(wsb + L::kKI + (static_cast<size_t>(16 * t + lr) * D + 32 * ks + 8 * grp) * 2) =
+                *reinterpret_cast<bf16x8*>(wsb + L::kKI + (static_cast<size_t>(16 * t + lr) * DK + 32 * ks + 8 * grp) * 2) =
                     kf[t][ks];
-        store_v_image<L, D>(v, wsb, t0, nvalid, H, h, lane);
+        store_v_image<L, DV>(v, wsb, t0, nvalid, H, h, lane);
     }
     __syncthreads();
 
@@ -524,7 +527,7 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                *reinterpret_cast<bf16x8*>(wsb + L::kQI + (static_cast<size_t>(16 * t + lr) * D + 32 * ks + 8 * grp) * 2) =
+                *reinterpret_cast<bf16x8*>(wsb + L::kQI + (static_cast<size_t>(16 * t + lr) * DK + 32 * ks + 8 * grp) * 2) =
                     qp[t][ks];
     }
 
@@ -579,7 +582,7 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
 // the diagonal tile each half spans at most 8 tokens of decay, so the
 // operands stay in range while the log-gates of 8 consecutive tokens sum to
 // more than -80 on every key row.  The walk over the key axis goes in steps
-// of 32 keys, so that only 32 of the D gates per row are live at a time:
+// of 32 keys, so that only 32 of the DK gates per row are live at a time:
 // the cumulative gates G of the step are an inclusive scan over the chunk's
 // rows (16 lanes hold 16 rows; the totals of earlier row tiles are added).
 // ---------------------------------------------------------------------------
@@ -605,14 +608,14 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
     return as_bf16x8(u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])});
 }
 
-template <int D, bool F32>
+template <int DK, int DV, bool F32>
 __global__ void __launch_bounds__(64)
 prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const void* __restrict__ v, const float* __restrict__ g,
                         const float* __restrict__ beta, char* __restrict__ ws, SeqGeom geo, int H,
                         int Hqk, int group, bool tiled) {
-    using L = WsL<D, true, F32>;
-    constexpr int KS = D / 32;
+    using L = WsL<DK, DV, true, F32>;
+    constexpr int KS = DK / 32;
     __shared__ __attribute__((aligned(16))) float sA[kC][kC];
     __shared__ float sBeta[kC];
 
@@ -633,7 +636,7 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
     char* wsb = ws + static_cast<size_t>(blk) * L::kBlock;
 
     sBeta[lane] = lane < nvalid ? beta[(static_cast<size_t>(t0) + lane) * H + h] : 0.f;
-    if constexpr (F32) store_v_image<L, D>(v, wsb, t0, nvalid, H, h, lane);
+    if constexpr (F32) store_v_image<L, DV>(v, wsb, t0, nvalid, H, h, lane);
 
     // pair p = mt (mt + 1) / 2 + nt of row tile mt and column tile nt <= mt
     f32x4 accA[10], accQ[10];
@@ -663,10 +666,10 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
             const int r = 16 * t + lr;
             if (r < nvalid) {
                 const size_t tok = static_cast<size_t>(t0) + r;
-                const f32x4 g0 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * D + d0);
-                const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * D + d0 + 4);
-                kb[t] = __builtin_bit_cast(u32x4, ld8_in<F32>(k, (tok * Hqk + hq) * D + d0));
-                qb[t] = __builtin_bit_cast(u32x4, ld8_in<F32>(q, (tok * Hqk + hq) * D + d0));
+                const f32x4 g0 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * DK + d0);
+                const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * DK + d0 + 4);
+                kb[t] = __builtin_bit_cast(u32x4, ld8_in<F32>(k, (tok * Hqk + hq) * DK + d0));
+                qb[t] = __builtin_bit_cast(u32x4, ld8_in<F32>(q, (tok * Hqk + hq) * DK + d0));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     G[t][j] = g0[j];
@@ -734,7 +737,7 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
                 const float dk = elem(kb[t], j) * __expf(GL[j] - G[t][j]);
                 sKT[8 * grp + j][16 * t + lr] = static_cast<uint16_t>(cvt2(dk, 0.f) & 0xffffu);
             }
-            const size_t off = (static_cast<size_t>(16 * t + lr) * D + d0) * 2;
+            const size_t off = (static_cast<size_t>(16 * t + lr) * DK + d0) * 2;
             *reinterpret_cast<bf16x8*>(wsb + L::kKG + off) = pack8(a);
             *reinterpret_cast<bf16x8*>(wsb + L::kQG + off) = pack8(b);
         }
@@ -742,13 +745,13 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
         for (int k16 = 0; k16 < 2; ++k16) {  // keys 32 ks + 16 k16 + lr
             const int i0 = 32 * ks + 16 * k16;
-            const int w = i0 / (D / 4), mt = (i0 % (D / 4)) / 16;  // the state wavefront and tile
+            const int w = i0 / (DK / 4), mt = (i0 % (DK / 4)) / 16;  // the state wavefront and tile
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2) {
                 const uint16_t* src = &sKT[16 * k16 + lr][32 * ks2 + 4 * grp];
                 const u32x2 lo4 = *reinterpret_cast<const u32x2*>(src);
                 const u32x2 hi4 = *reinterpret_cast<const u32x2*>(src + 16);
-                *reinterpret_cast<u32x4*>(wsb + L::kKDF + ((((w * (D / 64) + mt) * 2 + ks2) * 64 + lane) * 16)) =
+                *reinterpret_cast<u32x4*>(wsb + L::kKDF + ((((w * (DK / 64) + mt) * 2 + ks2) * 64 + lane) * 16)) =
                     u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
             }
         }
@@ -811,19 +814,19 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
 // chain: one workgroup (two wavefronts) per (sequence, head, 16-column block)
 // ---------------------------------------------------------------------------
 
-// LDS image of a K chunk: row-major [64][D] bf16 with the 16-byte pieces of
+// LDS image of a K chunk: row-major [64][DK] bf16 with the 16-byte pieces of
 // row r permuted by an XOR with sw(r), so that both the row reads of the
 // X = K S operand (16 rows, one piece each) and the transposing reads of the
 // K^T operand (8 rows, two adjacent pieces each) touch every bank once.
-template <int D>
+template <int DK>
 __device__ __forceinline__ int k_swz(int r) {
-    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    if constexpr (DK == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
     else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 // Element offset of (r, c) in the K image, c a multiple of 4.
-template <int D>
+template <int DK>
 __device__ __forceinline__ int k_at(int r, int c) {
-    return r * D + 8 * ((c >> 3) ^ k_swz<D>(r)) + (c & 7);
+    return r * DK + 8 * ((c >> 3) ^ k_swz<DK>(r)) + (c & 7);
 }
 
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at
@@ -849,14 +852,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
 // which covers the latency of the direct-to-LDS loads from memory; the V
 // block (four values per state lane) goes to registers instead, so that
 // four slots fit.
-template <int D, bool KDA>
+template <int DK, bool KDA>
 struct ChainLds {
     static constexpr int kImages = 2;
-    static constexpr int kE = 0;                           // gate block (Ws<D>::kE layout)
+    static constexpr int kE = 0;                           // gate block (Ws<DK>::kE layout)
     static constexpr int kK = kE + 1024;                   // K image (KDA: KG)
-    static constexpr int kQ = kK + kC * D * 2;             // Q image (KDA: QG)
-    static constexpr int kSlot = kK + kImages * kC * D * 2;
-    static constexpr int kLoads = 1 + kImages * (kC * D * 2 / 1024);  // 1 KiB loads per chunk
+    static constexpr int kQ = kK + kC * DK * 2;            // Q image (KDA: QG)
+    static constexpr int kSlot = kK + kImages * kC * DK * 2;
+    static constexpr int kLoads = 1 + kImages * (kC * DK * 2 / 1024);  // 1 KiB loads per chunk
     static constexpr int kRing = 4;
     static constexpr int kAhead = kRing - 1;  // chunks loaded ahead of the one in use
 };
@@ -871,25 +874,25 @@ __device__ __forceinline__ bf16x8 ld_split(const uint16_t* p0, const uint16_t* p
     return join(*reinterpret_cast<const u32x2*>(p0), *reinterpret_cast<const u32x2*>(p1));
 }
 
-template <int D, bool KDA, bool F32>
+template <int DK, int DV, bool KDA, bool F32>
 __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
                      float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
                      int Hqk, int group, bool tiled, int K, float* __restrict__ final_state) {
-    using L = WsL<D, KDA, F32>;
-    using M = ChainLds<D, KDA>;
+    using L = WsL<DK, DV, KDA, F32>;
+    using M = ChainLds<DK, KDA>;
     // K and Q come from the workspace's images for KDA and for float32
     // inputs, V for float32 inputs; otherwise straight from the bf16 inputs
     constexpr bool kImgKQ = KDA || F32;
     constexpr int kRing = M::kRing;
-    constexpr int NCB = D / 16;        // column blocks per head
+    constexpr int NCB = DV / 16;       // column blocks per head
     constexpr int KS = L::KS;          // k-steps over d_k
-    constexpr int SRW = D / 4;         // state rows per state wavefront
+    constexpr int SRW = DK / 4;        // state rows per state wavefront
     constexpr int SMT = SRW / 16;      // state tiles per state wavefront
-    constexpr int PPR = D / 8;         // 16-byte pieces per K row
+    constexpr int PPR = DK / 8;        // 16-byte pieces per K row
     constexpr int KPT = kC * PPR / 64; // 1 KiB loads of the K image
-    constexpr int SLD = D + 8;         // padded row of sS (bf16)
+    constexpr int SLD = DK + 8;        // padded row of sS (bf16)
     constexpr int CLD = kC + 8;        // padded row of sR, sW, sWp (bf16)
     constexpr int OLD = 20;            // padded row of sO (fp32)
 
@@ -935,8 +938,8 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // slot 0 of the sequence's K slots holds the start state; slots
         // 1..nsnap receive the state after that many tokens, and the final
         // state goes back to slot 0 when K == 1, else to final_state (if given)
-        float* st = state + static_cast<size_t>(bh) * K * D * D;
-        float* fin = K == 1 ? st : (final_state ? final_state + static_cast<size_t>(bh) * D * D : nullptr);
+        float* st = state + static_cast<size_t>(bh) * K * DK * DV;
+        float* fin = K == 1 ? st : (final_state ? final_state + static_cast<size_t>(bh) * DK * DV : nullptr);
         const int nsnap = K > 1 ? min(len, K - 1) : 0;
         // tile mt: d_k rows SRW w + 16 mt + 4 grp + 0..3 of column `col`
         f32x4 S[SMT];
@@ -944,7 +947,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                S[mt][rr] = st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * D + col];
+                S[mt][rr] = st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * DV + col];
         auto publish_state = [&]() {  // bf16 state rows -> sS (B operand of K S and Q S)
 #pragma unroll
             for (int mt = 0; mt < SMT; ++mt)
@@ -971,12 +974,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             int rowb, off0;
             if constexpr (F32) {  // the workspace's bf16 V image
                 rv = ws_rsrc(n);
-                rowb = D * 2;
+                rowb = DV * 2;
                 off0 = L::kVI + col * 2;
             } else {
-                const int row_b16 = H * D * 2;
-                rv = make_rsrc(v + (static_cast<size_t>(start + r0) * H + h) * D,
-                               (len - 1 - r0) * row_b16 + D * 2);
+                const int row_b16 = H * DV * 2;
+                rv = make_rsrc(v + (static_cast<size_t>(start + r0) * H + h) * DV,
+                               (len - 1 - r0) * row_b16 + DV * 2);
                 rowb = row_b16;
                 off0 = col * 2;
             }
@@ -994,7 +997,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     kt[mt][ks] = as_bf16x8(
-                        buf_ld16(rw, WsKda<D>::kKDF + (((w * SMT + mt) * 2 + ks) * 64 + lane) * 16));
+                        buf_ld16(rw, WsKda<DK>::kKDF + (((w * SMT + mt) * 2 + ks) * 64 + lane) * 16));
         };
         if constexpr (KDA) load_kt(0);
         publish_state();
@@ -1011,7 +1014,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             for (int ks = 0; ks < KS; ++ks) {
                 const int c = 32 * ks + 4 * grp;
                 const int r = 16 * w + lr;
-                X = mfma(ld_split(&sK[k_at<D>(r, c)], &sK[k_at<D>(r, c + 16)]),
+                X = mfma(ld_split(&sK[k_at<DK>(r, c)], &sK[k_at<DK>(r, c + 16)]),
                          ld_split(&sS[lr][c], &sS[lr][c + 16]), X);
             }
             // GDA: exp(G_r) for the rows of X, exp(G_last - G_r) for W', and
@@ -1065,7 +1068,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     for (int ks = 0; ks < 2; ++ks) {
                         const int r = 32 * ks + 4 * grp + (lr >> 2);
                         const int cc = SRW * w + 16 * mt + 4 * (lr & 3);
-                        kt[mt][ks] = join(ld_tr(&sK[k_at<D>(r, cc)]), ld_tr(&sK[k_at<D>(r + 16, cc)]));
+                        kt[mt][ks] = join(ld_tr(&sK[k_at<DK>(r, cc)]), ld_tr(&sK[k_at<DK>(r + 16, cc)]));
                     }
             }
             {
@@ -1094,17 +1097,17 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     const float a = E[kEs + r];
                     const float wv = __uint_as_float(static_cast<uint32_t>(sW[0][lr][r]) << 16) +
                                      __uint_as_float(static_cast<uint32_t>(sW[1][lr][r]) << 16);
-                    float* dst = st + static_cast<size_t>(n * kC + r + 1) * D * D;
+                    float* dst = st + static_cast<size_t>(n * kC + r + 1) * DK * DV;
 #pragma unroll
                     for (int mt = 0; mt < SMT; ++mt) {
                         const int i0 = SRW * w + 16 * mt + 4 * grp;
-                        const u32x2 kk = *reinterpret_cast<const u32x2*>(&sK[k_at<D>(r, i0)]);
+                        const u32x2 kk = *reinterpret_cast<const u32x2*>(&sK[k_at<DK>(r, i0)]);
                         const float kv[4] = {__uint_as_float(kk[0] << 16), __uint_as_float(kk[0] & 0xffff0000u),
                                              __uint_as_float(kk[1] << 16), __uint_as_float(kk[1] & 0xffff0000u)};
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) {
                             X[mt][rr] = fmaf(kv[rr], wv, a * X[mt][rr]);
-                            dst[static_cast<size_t>(i0 + rr) * D + col] = X[mt][rr];
+                            dst[static_cast<size_t>(i0 + rr) * DV + col] = X[mt][rr];
                         }
                     }
                 }
@@ -1139,7 +1142,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr)
-                    fin[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * D + col] = S[mt][rr];
+                    fin[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * DV + col] = S[mt][rr];
         }
         return;
     }
@@ -1168,7 +1171,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             for (int ks = 0; ks < KS; ++ks) {
                 const int c = 32 * ks + 4 * grp;
                 const int rq = 16 * w + lr;
-                P = mfma(ld_split(&sQ[k_at<D>(rq, c)], &sQ[k_at<D>(rq, c + 16)]),
+                P = mfma(ld_split(&sQ[k_at<DK>(rq, c)], &sQ[k_at<DK>(rq, c + 16)]),
                          ld_split(&sS[lr][c], &sS[lr][c + 16]), P);
             }
             f32x4 eg = {1.f, 1.f, 1.f, 1.f};  // KDA: the decay is inside QG
@@ -1210,9 +1213,9 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // reads come before chunk n's first barrier.
         const int l = wave - kStateWaves - kOutWaves;
         const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
-        const size_t headq0 = (static_cast<size_t>(start) * Hqk + hq) * D;  // q/k element (start, hq, 0)
-        const int rowq_b16 = Hqk * D * 2;                                   // bytes per token of q, k
-        const int seqq_b16 = (len - 1) * rowq_b16 + D * 2;  // end of the last valid row of q, k
+        const size_t headq0 = (static_cast<size_t>(start) * Hqk + hq) * DK;  // q/k element (start, hq, 0)
+        const int rowq_b16 = Hqk * DK * 2;                                   // bytes per token of q, k
+        const int seqq_b16 = (len - 1) * rowq_b16 + DK * 2;  // end of the last valid row of q, k
         constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
         // parts of kP01, kP01 and the rest: little is left for after B3, so
         // that a loader reaches B1 (after waiting for the next chunk) early
@@ -1222,9 +1225,9 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const int r0 = n * kC;
             const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
             const __amdgpu_buffer_rsrc_t rk =
-                make_rsrc(k + headq0 + static_cast<size_t>(r0) * Hqk * D, seqq_b16 - r0 * rowq_b16);
+                make_rsrc(k + headq0 + static_cast<size_t>(r0) * Hqk * DK, seqq_b16 - r0 * rowq_b16);
             const __amdgpu_buffer_rsrc_t rq =
-                make_rsrc(q + headq0 + static_cast<size_t>(r0) * Hqk * D, seqq_b16 - r0 * rowq_b16);
+                make_rsrc(q + headq0 + static_cast<size_t>(r0) * Hqk * DK, seqq_b16 - r0 * rowq_b16);
             const int j0 = qt * kP01, j1 = qt == 2 ? kPer : (qt + 1) * kP01;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
@@ -1237,10 +1240,10 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     const int pi = i - 1 - im * KPT;
                     const int p = 64 * pi + lane;  // image piece: row p / PPR, slot p % PPR
                     const int rr = p / PPR;
-                    const int piece = 16 * ((p % PPR) ^ k_swz<D>(rr));
-                    char* dst = slot + M::kK + im * (kC * D * 2) + 1024 * pi;
+                    const int piece = 16 * ((p % PPR) ^ k_swz<DK>(rr));
+                    char* dst = slot + M::kK + im * (kC * DK * 2) + 1024 * pi;
                     if constexpr (kImgKQ) {  // the workspace's row-major images
-                        dma16(rw, dst, (im == 0 ? L::kKI : L::kQI) + rr * (D * 2) + piece);
+                        dma16(rw, dst, (im == 0 ? L::kKI : L::kQI) + rr * (DK * 2) + piece);
                     } else {
                         dma16(im == 1 ? rq : rk, dst, rr * rowq_b16 + piece);
                     }
@@ -1273,7 +1276,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // ======================= storer wavefront ==========================
         // chunk n's output block from sO to o: lane -> row lane / 4 + 16 i,
         // columns 4 (lane % 4) + 0..3 of the block, read as two 8-byte halves
-        float* const obase = o + (static_cast<size_t>(start) * H + h) * D + cb * 16 + 4 * (lane & 3);
+        float* const obase = o + (static_cast<size_t>(start) * H + h) * DV + cb * 16 + 4 * (lane & 3);
         auto store_o = [&](int n, int i0) {  // rows 16 i + lane / 4, i = i0, i0 + 1
 #pragma unroll
             for (int i = i0; i < i0 + 2; ++i) {
@@ -1283,7 +1286,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 const f32x2 c = *reinterpret_cast<const f32x2*>(src + 2);
                 const int tok = n * kC + rr;  // token of the sequence
                 if (tok < len)
-                    *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * D) = f32x4{a[0], a[1], c[0], c[1]};
+                    *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * DV) = f32x4{a[0], a[1], c[0], c[1]};
             }
         };
         // half of the block after B1, half after B2: sO is rewritten after B3
@@ -1300,7 +1303,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D, bool KDA, bool F32>
+template <int DK, int DV, bool KDA, bool F32>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     char* ws = static_cast<char*>(a.workspace);
     SeqGeom geo;
@@ -1324,10 +1327,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     }
     const dim3 prep_grid(static_cast<unsigned>(a.H) * geo.CT);
     if (KDA)
-        hipLaunchKernelGGL((prefill_prep_kda_kernel<D, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k,
+        hipLaunchKernelGGL((prefill_prep_kda_kernel<DK, DV, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k,
                            a.v, a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     else
-        hipLaunchKernelGGL((prefill_prep_kernel<D, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k, a.v,
+        hipLaunchKernelGGL((prefill_prep_kernel<DK, DV, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k, a.v,
                            a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1337,7 +1340,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const auto* k = static_cast<const uint16_t*>(a.k);
     const auto* v = static_cast<const uint16_t*>(a.v);
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
-    hipLaunchKernelGGL((prefill_chain_kernel<D, KDA, F32>), dim3(bh * (D / 16)), dim3(kChainThreads), 0,
+    hipLaunchKernelGGL((prefill_chain_kernel<DK, DV, KDA, F32>), dim3(bh * (DV / 16)), dim3(kChainThreads), 0,
                        stream, q, k, v, a.state, a.o, ws, geo, a.H, a.Hqk, a.group, a.tiled, a.K,
                        a.final_state);
     return hipGetLastError();
@@ -1345,7 +1348,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 
 template <bool KDA, bool F32>
 static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
-    return a.d == 128 ? launch_prefill_t<128, KDA, F32>(a, stream) : launch_prefill_t<64, KDA, F32>(a, stream);
+    if (a.dk == 128)
+        return a.dv == 128 ? launch_prefill_t<128, 128, KDA, F32>(a, stream) : launch_prefill_t<128, 64, KDA, F32>(a, stream);
+    return a.dv == 128 ? launch_prefill_t<64, 128, KDA, F32>(a, stream) : launch_prefill_t<64, 64, KDA, F32>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
