@@ -1,4 +1,4 @@
-// gdn_prefill.hip -- chunked prefill of the GDA recurrence on bf16 MFMA (gfx950).
+// gdn_prefill.hip -- chunked prefill of the GDN recurrence on bf16 MFMA (gfx950).
 //
 // The pages enable a chunked fused GDN path for prompt processing (llama.cpp
 // commit log, tag b9752, bullet "llama : enable chunked fused GDN path") but
@@ -11,23 +11,33 @@
 //     O      = diag(exp G) Q S + QKm W
 //     S_next = exp(G_last) S + K^T (diag(exp(G_last - G)) W)
 // (equal to the token loop up to rounding; a short final chunk acts as if
-// padded with k = q = v = 0, beta = 0, g = 0).
+// padded with k = q = v = 0, beta = 0, g = 0).  With one log-gate per key row
+// (KDA, same page, bullet "metal : add Metal backend for
+// GGML_OP_GATED_DELTA_NET") the decays move inside the sums over keys: A and
+// QKm take exp(G_r[i] - G_s[i]) per key i, K and Q are used as K o exp(G) and
+// Q o exp(G), and the state carry is diag(exp G_last) S + (K o exp(G_last -
+// G))^T W.  The key and value head sizes DK and DV (64 or 128 each) are
+// separate template parameters: the state is DK x DV.
 //
-// Two kernels:
+// Two kernels (plus, for packed sequences of different lengths, a
+// one-wavefront table of sanitised offsets):
 //  prep  (one wavefront per chunk and head, all chunks in parallel): G,
 //        K K^T and Q K^T on MFMA, the gate masks, the unit lower triangular
 //        inverse T by forward substitution in fp32.  It writes T1 and QKm to
 //        the workspace as ready-made MFMA A operands (bf16 hi + lo pairs,
 //        x = hi + lo to ~2^-17), in the order the chain kernel reads them,
-//        plus the gate factors.
+//        plus the gate factors; for KDA also the decayed K and Q images and
+//        the state update's operand fragments, and for float32 q/k/v the
+//        bf16 images of K, Q and V.
 //  chain (one workgroup per head and 16 state columns, serial over chunks):
-//        four state wavefronts hold the d_k x 16 fp32 state block in MFMA
+//        four state wavefronts hold the DK x 16 fp32 state block in MFMA
 //        accumulators and per chunk form X = K S, R = V - exp(G) X, W = T1 R
 //        and S <- exp(G_last) S + K^T (exp(G_last - G) W), exchanging R, W
-//        and the bf16 state through LDS (three barriers per chunk); four
-//        output wavefronts form O = exp(G) Q S + QKm W alongside;
-//        loader wavefronts fill a three-chunk LDS ring with direct-to-LDS
-//        loads two chunks ahead, and a storer wavefront writes O.
+//        and the bf16 state through LDS (three barriers per chunk), and
+//        write the K-slot snapshots that fall in the chunk; four output
+//        wavefronts form O = exp(G) Q S + QKm W alongside; four loader
+//        wavefronts fill a four-slot LDS ring with direct-to-LDS loads three
+//        chunks ahead, and a storer wavefront writes O.
 //        Products whose rounding would reach the carried state or the output
 //        visibly use hi/lo operand pairs (T1 R, QKm W, K^T W').
 //
