@@ -94,3 +94,52 @@ def test_prefill_rejects_kda_and_fp32():
     s = d["state"][:, :, 0].contiguous()
     with pytest.raises(Exception):
         _gdn().gdn_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], s)
+
+
+def test_prefill_graph_replay_matches_eager():
+    """The bench times HIP-graph replays of the prefill: every replay must
+    equal the eager result bit for bit, with eager work between replays.
+    Covers the uniform, variable-length (its offset table is rebuilt by a
+    kernel on every call) and KDA prefills."""
+    gdn = _gdn()
+    c = gi.make_case(1, 200, 4, 128, qkv_dtype="bf16", seed=41)
+    ck = gi.make_case(1, 150, 2, 64, gate="kda", qkv_dtype="bf16", seed=42)
+    vc = gi.make_varlen_case([70, 0, 130], 4, 64, seed=43)
+    u, uk = upload(c), upload(ck)
+    bf = torch.bfloat16
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    vq, vk, vv, vg, vb = t(vc.q, bf), t(vc.k, bf), t(vc.v, bf), t(vc.g), t(vc.beta)
+    vcu = t(vc.cu_seqlens, torch.int32)
+    s0, sk0, sv0 = (u["state"][:, :, 0].contiguous(), uk["state"][:, :, 0].contiguous(), t(vc.state))
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(1, 200, 4, 128, 128), dtype=torch.uint8, device="cuda")
+    wsk = torch.empty(gdn.gdn_prefill_kda_workspace_size(1, 150, 2, 64, 64), dtype=torch.uint8, device="cuda")
+    wsv = torch.empty(gdn.gdn_prefill_varlen_workspace_size(3, vc.total, 4, 64, 64), dtype=torch.uint8,
+                      device="cuda")
+    s, sk, sv = torch.empty_like(s0), torch.empty_like(sk0), torch.empty_like(sv0)
+    o = torch.empty((1, 200, 4, 128), device="cuda")
+    ok = torch.empty((1, 150, 2, 64), device="cuda")
+    ov = torch.zeros((vc.total, 4, 64), device="cuda")
+
+    def run():
+        torch.mul(s0, 1.0, out=s)  # reset the states with kernels (x * 1 is exact)
+        torch.mul(sk0, 1.0, out=sk)
+        torch.mul(sv0, 1.0, out=sv)
+        gdn.gdn_prefill_chunked(u["q"], u["k"], u["v"], u["g"], u["beta"], s, o=o, workspace=ws)
+        gdn.gdn_prefill_chunked_kda(uk["q"], uk["k"], uk["v"], uk["g"], uk["beta"], sk, o=ok, workspace=wsk)
+        gdn.gdn_prefill_chunked_varlen(vcu, vq, vk, vv, vg, vb, sv, o=ov, workspace=wsv)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [bits(x) for x in (o, s, ok, sk, ov[:70], ov[70:], sv)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for _ in range(3):
+        for x in (o, s, ok, sk, sv, ov, ws, wsk, wsv):
+            x.fill_(0 if x.dtype == torch.uint8 else float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [bits(x) for x in (o, s, ok, sk, ov[:70], ov[70:], sv)]
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b)
