@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "3144bf48ee78d74c90ecdd8e155bd5aa5d5e406c39942e9a646ae4a7474f67ae",
+    "sha256": "3e658bacc23f31b1b7c15a3419cffd10e9847bee2381caf68728b647ba445e83",
     "fetch_kib": 33508.59375,       # median over 62 decode dispatches
-    "write_kib": 66079.125,
+    "write_kib": 66077.375,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
