@@ -23,7 +23,8 @@
 // one-wavefront table of sanitised offsets):
 //  prep  (one wavefront per chunk and head, all chunks in parallel): G,
 //        K K^T and Q K^T on MFMA, the gate masks, the unit lower triangular
-//        inverse T by forward substitution in fp32.  It writes T1 and QKm to
+//        inverse T in fp32 by 16 x 16 blocks (forward substitution on the
+//        diagonal, block substitution on fp32 MFMA below).  It writes T1 and QKm to
 //        the workspace as ready-made MFMA A operands (bf16 hi + lo pairs,
 //        x = hi + lo to ~2^-17), in the order the chain kernel reads them,
 //        plus the gate factors; for KDA also the decayed K and Q images and
@@ -324,75 +325,127 @@ prefill_table_kernel(const int32_t* __restrict__ cu, int N, int total, int32_t* 
 // ---------------------------------------------------------------------------
 // prep: one wavefront per (sequence, head, chunk)
 // ---------------------------------------------------------------------------
-// T = (I + A)^-1 diag(beta) for one chunk, from A (strict lower part, fp32,
-// in sA) and beta (sBeta), written to the workspace block as T1F; sA is
-// reused for the transpose.  Called by the whole (one-wavefront) block after
-// a barrier that publishes A.
+// Row pitch of the fp32 A matrix in LDS: 4 floats of padding move each row
+// by 4 banks, so that 16 rows read at one column offset meet distinct banks.
+constexpr int kAP = kC + 4;
+
+__device__ __forceinline__ f32x4 mfma_f32(f32x4 acc, const f32x4& a, const f32x4& b) {
+    // k = 4 (l / 16) + s at step s: lane l gives a[s] = X[l % 16][k] and
+    // b[s] = Y[k][l % 16], so 4 steps sum X Y over k = 0..15 with the
+    // operands in the layout of an MFMA result
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// T1 = (I + A)^-1 diag(beta) for one chunk, from A (strict lower part, fp32,
+// pitch kAP, in sA) and beta (sBeta), written to the workspace block as T1F.
+// With I + A in 16 x 16 blocks and D_b the inverse of diagonal block b, the
+// inverse T has T_bb = D_b and, below the diagonal (block substitution),
+//   T_ij = -D_i (A_ij D_j + sum_{j<k<i} A_ik T_kj).
+// The D_b come from forward substitution in fp32 (16 lanes per block, one
+// column each) and the blocks below the diagonal from fp32 MFMA 16x16x4
+// products.  A 16 x 16 MFMA result holds rows 4 (l / 16) + 0..3 of column
+// l % 16 in lane l.  Blocks of T that later products take as right factor
+// are formed that way (T_ij = D_i P, with P = -(A_ij D_j + ...)); every
+// block below the diagonal is also formed transposed (P^T D_i^T), which puts
+// row l % 16, columns 4 (l / 16) + 0..3 in lane l: the split-order A operand
+// layout of T1F.  The upper blocks of sA (never written with A) keep the D_b.
+// Called by the whole (one-wavefront) block after a barrier that publishes A.
 template <class L>
-__device__ __forceinline__ void solve_store_t1(float (*sA)[kC], const float* sBeta, char* wsb,
+__device__ __forceinline__ void solve_store_t1(float (*sA)[kAP], const float* sBeta, char* wsb,
                                                int lane) {
-    uint16_t (*sT)[kC][kC] = reinterpret_cast<uint16_t (*)[kC][kC]>(&sA[0][0]);
-    // 8-byte unit u of row r of the transpose is kept at unit u ^ tsw(r), so
-    // that the split-order reads below (16 rows, two units each) meet every
-    // bank once.
-    auto tsw = [](int r) { return 2 * ((r >> 1) & 7); };
     const int lr = lane & 15;
     const int grp = lane >> 4;
-    // T = (I + A)^-1 by forward substitution, one column per lane, in fp32,
-    // in blocks of 16 rows: first the contributions of all earlier blocks
-    // (16 independent sums), then the sequential triangle of the block.
-    float x[kC];
-#pragma unroll
-    for (int I = 0; I < kC / 16; ++I) {
-        float y[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = (16 * I + i == lane) ? 1.f : 0.f;
-#pragma unroll
-        for (int s4 = 0; s4 < 16 * I; s4 += 4) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * I + i][s4]);
-                y[i] = fmaf(-av.x, x[s4], y[i]);
-                y[i] = fmaf(-av.y, x[s4 + 1], y[i]);
-                y[i] = fmaf(-av.z, x[s4 + 2], y[i]);
-                y[i] = fmaf(-av.w, x[s4 + 3], y[i]);
-            }
-        }
+    // D_b is kept in upper block (0, b + 1) of sA for b < 3, D_3 in (1, 2)
+    auto drow = [](int b) { return b == 3 ? 16 : 0; };
+    auto dcol = [](int b) { return b == 3 ? 32 : 16 * (b + 1); };
+    {
+        // column lr of D_grp: forward substitution over the block's 16 rows
+        const int b = grp;
+        float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float acc = y[i];
+            float acc = (i == lr) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 16 * I; s < 16 * I + i; ++s) acc = fmaf(-sA[16 * I + i][s], x[s], acc);
-            x[16 * I + i] = acc;
+            for (int s4 = 0; 4 * s4 < i; ++s4) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[16 * b + i][16 * b + 4 * s4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * s4 + e < i) acc = fmaf(-av[e], x[4 * s4 + e], acc);
+            }
+            x[i] = acc;
         }
-    }
-
-    // T1 = T diag(beta): this lane's column, split hi/lo, transposed through
-    // LDS (A is no longer read) into split-order A operands.
-    __syncthreads();  // every read of A is done before its storage is reused
-    const float bcol = sBeta[lane];
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-        uint32_t hi, lo;
-        split_bf16(x[r] * bcol, hi, lo);
-        const int c = 4 * ((lane >> 2) ^ tsw(r)) + (lane & 3);
-        sT[0][r][c] = static_cast<uint16_t>(hi);
-        sT[1][r][c] = static_cast<uint16_t>(lo);
+        for (int i = 0; i < 16; ++i) sA[drow(b) + i][dcol(b) + lr] = x[i];
     }
-    __syncthreads();
+    __syncthreads();  // the D_b are published
+
+    // row lr, columns 4 grp + 0..3 of the block at (r0, c0): A operand of X in X Y
+    auto rows = [&](int r0, int c0) {
+        return *reinterpret_cast<const f32x4*>(&sA[r0 + lr][c0 + 4 * grp]);
+    };
+    // rows 4 grp + 0..3 of column lr of D_b: B operand of D_b in X D_b
+    auto dcolumn = [&](int b) {
+        f32x4 v;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] = sA[drow(b) + 4 * grp + s][dcol(b) + lr];
+        return v;
+    };
+    auto neg = [](const f32x4& v) { return f32x4{-v[0], -v[1], -v[2], -v[3]}; };
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 Dr[4], Dc[3];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Dr[b] = rows(drow(b), dcol(b));
+#pragma unroll
+    for (int b = 0; b < 3; ++b) Dc[b] = dcolumn(b);
+
+    // Tt[i][j]: block (i, j) of T as row lr, columns 4 grp + 0..3
+    f32x4 Tt[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Tt[i][j] = i == j ? Dr[i] : z;
+    // column block 0
+    f32x4 Pn = neg(mfma_f32(z, rows(16, 0), Dc[0]));
+    const f32x4 T10 = mfma_f32(z, Dr[1], Pn);
+    Tt[1][0] = mfma_f32(z, Pn, Dr[1]);
+    Pn = neg(mfma_f32(mfma_f32(z, rows(32, 0), Dc[0]), rows(32, 16), T10));
+    const f32x4 T20 = mfma_f32(z, Dr[2], Pn);
+    Tt[2][0] = mfma_f32(z, Pn, Dr[2]);
+    Pn = neg(mfma_f32(mfma_f32(mfma_f32(z, rows(48, 0), Dc[0]), rows(48, 16), T10), rows(48, 32), T20));
+    Tt[3][0] = mfma_f32(z, Pn, Dr[3]);
+    // column block 1
+    Pn = neg(mfma_f32(z, rows(32, 16), Dc[1]));
+    const f32x4 T21 = mfma_f32(z, Dr[2], Pn);
+    Tt[2][1] = mfma_f32(z, Pn, Dr[2]);
+    Pn = neg(mfma_f32(mfma_f32(z, rows(48, 16), Dc[1]), rows(48, 32), T21));
+    Tt[3][1] = mfma_f32(z, Pn, Dr[3]);
+    // column block 2
+    Pn = neg(mfma_f32(z, rows(48, 32), Dc[2]));
+    Tt[3][2] = mfma_f32(z, Pn, Dr[3]);
+
+    // T1 = T diag(beta), split hi/lo, as split-order A operands: k-step ks
+    // of row tile t takes columns 4 grp + 0..3 of blocks 2 ks and 2 ks + 1
+    f32x4 bt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bt[j] = *reinterpret_cast<const f32x4*>(&sBeta[16 * j + 4 * grp]);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x2 hi[2], lo[2];
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                const int r = 16 * t + lr;
-                const int u = 8 * ks + grp;  // 8-byte unit of columns 32 ks + 4 grp + 0..3
-                const u32x2 a = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * (u ^ tsw(r))]);
-                const u32x2 c = *reinterpret_cast<const u32x2*>(&sT[hl][r][4 * ((u + 4) ^ tsw(r))]);
-                *reinterpret_cast<u32x4*>(wsb + L::kT1F + frag_off(t, ks, hl, lane)) =
-                    u32x4{a[0], a[1], c[0], c[1]};
+            for (int half = 0; half < 2; ++half) {
+                const int j = 2 * ks + half;
+                const f32x4 v = Tt[t][j];
+                split4(v[0] * bt[j][0], v[1] * bt[j][1], v[2] * bt[j][2], v[3] * bt[j][3], hi[half], lo[half]);
             }
+            *reinterpret_cast<u32x4*>(wsb + L::kT1F + frag_off(t, ks, 0, lane)) =
+                u32x4{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+            *reinterpret_cast<u32x4*>(wsb + L::kT1F + frag_off(t, ks, 1, lane)) =
+                u32x4{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+        }
 }
 
 // Eight consecutive elements of a q/k/v row as one bf16 MFMA operand: bf16
@@ -437,9 +490,9 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
     constexpr int KS = L::KS;
     // A (fp32) during the solve, then the hi/lo transpose of T1 (bf16); a
     // barrier separates the two uses.
-    __shared__ __attribute__((aligned(16))) float sA[kC][kC];
+    __shared__ __attribute__((aligned(16))) float sA[kC][kAP];
     __shared__ float sG[kC];
-    __shared__ float sBeta[kC];
+    __shared__ __attribute__((aligned(16))) float sBeta[kC];
 
     const int lane = threadIdx.x;
     const int blk = blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
@@ -626,8 +679,8 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         int Hqk, int group, bool tiled) {
     using L = WsL<DK, DV, true, F32>;
     constexpr int KS = DK / 32;
-    __shared__ __attribute__((aligned(16))) float sA[kC][kC];
-    __shared__ float sBeta[kC];
+    __shared__ __attribute__((aligned(16))) float sA[kC][kAP];
+    __shared__ __attribute__((aligned(16))) float sBeta[kC];
 
     const int lane = threadIdx.x;
     const int blk = blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
