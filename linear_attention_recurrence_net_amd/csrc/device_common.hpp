@@ -9,6 +9,7 @@ namespace gdn {
 constexpr int kWave = 64;  // CDNA4 wavefront width (single target: gfx950)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
@@ -18,6 +19,14 @@ __device__ __forceinline__ f32x4 ld4_nt(const float* p) {
 }
 __device__ __forceinline__ void st4_nt(float* p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+// Workgroup barrier for data written to LDS with ds_write: waits for this
+// wavefront's LDS operations only, so that outstanding global and
+// direct-to-LDS loads and global stores stay in flight across it.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // bfloat16 bits -> float32 (exact).

@@ -63,7 +63,6 @@ namespace {
 constexpr int kC = 64;  // chunk length
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -190,15 +189,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// Workgroup barrier for data written to LDS with ds_write: waits for this
-// wavefront's LDS operations only, so that outstanding global and
-// direct-to-LDS loads (the prefetch of later chunks, read only by the
-// wavefront that issued them) stay in flight across it.  The memory clobber
-// keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Wait until at most N of this wavefront's global and direct-to-LDS loads

@@ -7,21 +7,24 @@
 //
 // Work mapping (HBM-bound: one read and one write of each fp32 state tile
 // dominate the bytes):
-//  * columns of S evolve independently, so each wavefront owns a block of
-//    CPW state columns across all d_k rows and needs no communication with
-//    other wavefronts (the pages' CUDA kernel shards columns across warps
-//    for the same register-pressure reason: llama.cpp commit log, tag b9752,
-//    bullet "Shard columns across warps");
-//  * a workgroup holds WPG such wavefronts of one (sequence, head);
-//  * inside a wavefront, lane = CG * rowgroup + colgroup with CG = CPW/4:
-//    the lane holds 4 consecutive columns (one 128-bit load per row) of
-//    RPL = d_k / (64/CG) consecutive rows;
-//  * the whole column block is loaded before the first token, so every lane
-//    has RPL independent 128-bit loads in flight;
+//  * one workgroup per (sequence, head); its WPH wavefronts split the d_k
+//    state rows into blocks of RW = d_k / WPH whole rows (all d_v columns);
+//  * inside a wavefront, lane = CG * sub + cg with CG = d_v / 4 lanes across
+//    a row (4 consecutive columns each, one 128-bit access) and RS = 64 / CG
+//    row sub-groups; sub-group `sub` holds the L = RW / RS consecutive rows
+//    sub * L .. sub * L + L - 1 of the block.  One load instruction thus
+//    moves RS whole rows of 4 * d_v bytes, and a lane's k and q rows are
+//    contiguous.  (A copy of a 64 MiB state in this order ran 4.5% faster
+//    on the MI355X than in column blocks of 128-byte row pieces.);
+//  * the whole row block is loaded before the first token, so every lane
+//    has L independent 128-bit loads in flight;
 //  * the decay is folded into the reductions (k' = a.k, q' = a.q, applied
 //    once on the update), so S is read from registers once per token;
-//  * S^T k' and S^T q' are summed inside the lane over its rows, then across
-//    the row groups with swizzle / DPP / permlane butterflies (no LDS).
+//  * S^T k' and S^T q' are summed inside the lane over its rows, across the
+//    row sub-groups with permlane butterflies, and across the wavefronts of
+//    the head through LDS (one LDS-only barrier per token, two buffers by
+//    token parity).  Every wavefront adds the partial sums in the same order,
+//    so all of them hold bit-identical totals.
 //
 // Per token the arithmetic is (folded form, equal to decay -> delta ->
 // readout):   u = S^T (a.k), p = S^T (a.q), w = beta (v - u),
@@ -30,55 +33,56 @@
 #include "device_common.hpp"
 #include "gdn_internal.hpp"
 
-// Tuning knobs (columns per wavefront, wavefronts per workgroup, minimum
-// waves per SIMD requested from the register allocator, streaming loads).
-#ifndef GDN_DEC_CPW
-#define GDN_DEC_CPW 32
-#endif
-#ifndef GDN_DEC_WPG
-#define GDN_DEC_WPG 2
-#endif
-#ifndef GDN_DEC_WAVES_PER_EU
-#define GDN_DEC_WAVES_PER_EU 0
-#endif
+#include <type_traits>
+
+// Tuning knobs (streaming loads and stores; wavefronts per head for one and
+// for several tokens).
 #ifndef GDN_DEC_NT_LOAD
 #define GDN_DEC_NT_LOAD 1
 #endif
 #ifndef GDN_DEC_NT_STORE
 #define GDN_DEC_NT_STORE 1
 #endif
+#ifndef GDN_DEC_WPH_ONE
+#define GDN_DEC_WPH_ONE 2
+#endif
+#ifndef GDN_DEC_WPH_MULTI
+#define GDN_DEC_WPH_MULTI 2
+#endif
+#ifndef GDN_DEC_WPH_MULTI_128
+#define GDN_DEC_WPH_MULTI_128 4
+#endif
 
 namespace gdn {
 
 namespace {
 
-constexpr int kCPW = GDN_DEC_CPW;
+// One head's d_k x d_v state tile, read and written through a buffer
+// resource: each lane keeps one byte offset, the 4 KiB windows of rows are
+// reached through the scalar offset, and the rows inside a window through
+// the instruction's immediate offset.  (Flat addressing would spend a 64-bit
+// address per row beyond the first 4 KiB.)  Accesses are streaming
+// (non-temporal) unless the tuning knobs say otherwise.
+template <int DK, int DV>
+struct TileIO {
+    static constexpr int WIN = 1024 / DV;  // rows per 4 KiB window
+    static constexpr int CP = 2;           // cache policy: nt
+    __amdgpu_buffer_rsrc_t r;
 
-// Wavefronts per workgroup (each owns kCPW state columns): GDN_DEC_WPG for
-// the single-token decode, twice that for launches over several tokens,
-// where the longer-lived workgroups measured faster (16-token-head verify at
-// d = 128: 25.3 us against 26.5 us), both capped by the column count.
-template <int DV, bool ONE>
-constexpr int waves_per_group() {
-    constexpr int want = ONE ? GDN_DEC_WPG : 2 * GDN_DEC_WPG;
-    return (DV / kCPW) < want ? (DV / kCPW) : want;
-}
+    __device__ __forceinline__ explicit TileIO(float* tile)
+        : r(__builtin_amdgcn_make_buffer_rsrc(tile, 0, DK * DV * 4, 0x00020000)) {}
 
-__device__ __forceinline__ f32x4 load_state(const float* p) {
-#if GDN_DEC_NT_LOAD
-    return ld4_nt(p);
-#else
-    return ld4(p);
-#endif
-}
-
-__device__ __forceinline__ void store_state(float* p, f32x4 v) {
-#if GDN_DEC_NT_STORE
-    st4_nt(p, v);
-#else
-    st4(p, v);
-#endif
-}
+    // row i of this lane's block; off = byte offset of the lane's first row
+    __device__ __forceinline__ f32x4 load(uint32_t off, int i) const {
+        return __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + (i % WIN) * DV * 4, (i / WIN) * 4096,
+                                                         GDN_DEC_NT_LOAD ? CP : 0));
+    }
+    __device__ __forceinline__ void store(uint32_t off, int i, f32x4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off + (i % WIN) * DV * 4,
+                                               (i / WIN) * 4096, GDN_DEC_NT_STORE ? CP : 0);
+    }
+};
 
 // The inputs one lane needs for one token: its RPL rows of k and q, its 4
 // columns of v, beta, and the log-gate (one, or RPL for per-row gates).
@@ -169,70 +173,100 @@ struct TokenRaw {
 
 }  // namespace
 
-// ONE: the launch has exactly one token and no snapshot (plain decode); the
-// token loop is then straight-line code.  DK and DV: key and value head
-// sizes (state rows and columns).
-template <int DK, int DV, bool KDA, bool BF16, bool ONE>
-__global__ void __launch_bounds__((waves_per_group<DV, ONE>() * kWave))
-#if GDN_DEC_WAVES_PER_EU > 0
-__attribute__((amdgpu_waves_per_eu(GDN_DEC_WAVES_PER_EU)))
-#endif
+// Sum of x over the lanes that share lane % FROM (the row sub-groups of a
+// wavefront): butterflies over lane bits log2(FROM)..5.
+template <int FROM>
+__device__ __forceinline__ float sum_subgroups(float x) {
+    static_assert(FROM == 16 || FROM == 32, "row width of 64 or 128 columns");
+    if constexpr (FROM == 16) x = add_xor16(x);
+    return add_xor32(x);
+}
+
+// ONE: the launch has exactly one token and no snapshot (plain decode).
+// DK and DV: key and value head sizes (state rows and columns).  WPH:
+// wavefronts per head, one workgroup per head.  Two wavefronts per SIMD are
+// requested (at most 256 registers), so a 1024-head decode grid of 2048
+// wavefronts is resident at once.
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH>
+__global__ void __launch_bounds__((WPH * kWave)) __attribute__((amdgpu_waves_per_eu(2)))
 recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const float* __restrict__ g,
                  const float* __restrict__ beta, float* __restrict__ state,
                  float* __restrict__ final_state, float* __restrict__ o, int T, int H, int K,
                  int n_snap, int Hqk, int group, bool tiled) {
-    constexpr int CG = kCPW / 4;     // lanes across one row segment
-    constexpr int RG = kWave / CG;   // row groups
-    constexpr int RPL = DK / RG;     // rows held per lane
-    constexpr int WPG = waves_per_group<DV, ONE>();
-    constexpr int NB = DV / (kCPW * WPG);  // workgroups per head
+    constexpr int CG = DV / 4;        // lanes across one state row
+    constexpr int RS = kWave / CG;    // row sub-groups (rows per load instruction)
+    constexpr int RW = DK / WPH;      // rows per wavefront
+    constexpr int L = RW / RS;        // rows per lane
+    constexpr int RED = 2 * DV + 4;   // one wavefront's partial sums in LDS: u, p, k.q
     constexpr size_t TILE = static_cast<size_t>(DK) * DV;
-    static_assert(RPL >= 1 && DK % RG == 0 && DV % (kCPW * WPG) == 0, "tiling");
+    static_assert(L >= 4 && L % 4 == 0 && RW % RS == 0 && DK % WPH == 0, "tiling");
+
+    // partial sums of each wavefront, two buffers by token parity
+    __shared__ __attribute__((aligned(16))) float red[WPH > 1 ? 2 * WPH * RED : 4];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
     const int cg = lane % CG;
-    const int rg = lane / CG;
-    const int bh = blockIdx.x / NB;  // b * H + h
-    const int cb = blockIdx.x - bh * NB;
-    const int col0 = (cb * WPG + wave) * kCPW + cg * 4;
-    const int row0 = rg * RPL;
+    const int sub = lane / CG;
+    const int bh = blockIdx.x;  // b * H + h
+    const int col0 = cg * 4;
+    const int row0 = wave * RW + sub * L;
     const int b = bh / H;
     const int h = bh - b * H;
     const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
 
     float* slots = state + static_cast<size_t>(bh) * K * TILE;
+    const uint32_t off0 = static_cast<uint32_t>(row0 * DV + col0) * 4u;  // byte offset in a tile
 
-    f32x4 s[RPL];
+    f32x4 s[L];
+    {
+        const TileIO<DK, DV> in(slots);
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) s[i] = load_state(slots + static_cast<size_t>(row0 + i) * DV + col0);
+        for (int i = 0; i < L; ++i) s[i] = in.load(off0, i);
+    }
 
     // Raw inputs of one token, as loaded (bf16 stays packed until used).
-    using Raw = TokenRaw<RPL, KDA, BF16>;
+    using Raw = TokenRaw<L, KDA, BF16>;
     const int n_tok = ONE ? 1 : T;
     Raw cur;
     if (n_tok > 0)
         cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h,
                  (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, DK, DV);
+    // The first token needs the whole row block and its own inputs, so wait
+    // for them here.  Without this wait the loop head would see the first
+    // token's input registers as still loading on every iteration; the
+    // memory counter is in order, so the wait it then emits there would also
+    // drain the previous token's snapshot stores.  After it, the in-loop
+    // waits cover only the prefetched inputs and the stores stay in flight.
+    if (!ONE) __builtin_amdgcn_s_waitcnt(0);
 
-    for (int t = 0; t < n_tok; ++t) {
+    // One token: the folded update of the row block, the readout, and (SNAP)
+    // the store of the new state to slot t + 1.  The body has no branch, so
+    // the wait the compiler places for the prefetched inputs counts exactly
+    // the stores issued after them and leaves those in flight.
+    auto step = [&](int t, auto snap_tag) {
+        constexpr bool SNAP = decltype(snap_tag)::value;
         const size_t bth = (static_cast<size_t>(b) * T + t) * H + h;
         const size_t bthq = (static_cast<size_t>(b) * T + t) * Hqk + hq;
-        // prefetch the next token while this one is computed
+        // prefetch the next token while this one is computed (the last token
+        // reloads itself, so the load needs no branch)
         Raw nxt;
-        if (!ONE && t + 1 < n_tok) nxt.load(q, k, v, g, beta, bth + H, bthq + Hqk, row0, col0, DK, DV);
+        if constexpr (!ONE) {
+            const int dn = t + 1 < n_tok ? 1 : 0;
+            nxt.load(q, k, v, g, beta, bth + dn * H, bthq + dn * Hqk, row0, col0, DK, DV);
+        }
 
-        float kv[RPL], qv[RPL];
+        float kv[L], qv[L];
         cur.unpack_kq(kv, qv);
         const f32x4 vv = cur.vvec();
         const float bt = cur.beta;
 
-        float a_row[KDA ? RPL : 1];
+        float a_row[KDA ? L : 1];
         float a_head = 1.0f;
         if constexpr (KDA) {
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) a_row[i] = expf(cur.g[i]);
+            for (int i = 0; i < L; ++i) a_row[i] = expf(cur.g[i]);
         } else {
             a_head = expf(cur.g[0]);
         }
@@ -242,7 +276,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
         float kq = 0.f;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
+        for (int i = 0; i < L; ++i) {
             float kk = kv[i], qq = qv[i];
             kq = fmaf(kv[i], qv[i], kq);
             if constexpr (KDA) {
@@ -258,15 +292,38 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
             p2 = fmaf(s[i].z, qq, p2);
             p3 = fmaf(s[i].w, qq, p3);
         }
-        u0 = sum_lanes_from<CG>(u0);
-        u1 = sum_lanes_from<CG>(u1);
-        u2 = sum_lanes_from<CG>(u2);
-        u3 = sum_lanes_from<CG>(u3);
-        p0 = sum_lanes_from<CG>(p0);
-        p1 = sum_lanes_from<CG>(p1);
-        p2 = sum_lanes_from<CG>(p2);
-        p3 = sum_lanes_from<CG>(p3);
-        kq = sum_lanes_from<CG>(kq);
+        // across the row sub-groups of the wavefront
+        u0 = sum_subgroups<CG>(u0);
+        u1 = sum_subgroups<CG>(u1);
+        u2 = sum_subgroups<CG>(u2);
+        u3 = sum_subgroups<CG>(u3);
+        p0 = sum_subgroups<CG>(p0);
+        p1 = sum_subgroups<CG>(p1);
+        p2 = sum_subgroups<CG>(p2);
+        p3 = sum_subgroups<CG>(p3);
+        kq = sum_subgroups<CG>(kq);
+        // across the wavefronts of the head: every lane writes its (equal)
+        // sub-group totals, then sums the wavefronts' partials in order 0..WPH-1
+        if constexpr (WPH > 1) {
+            float* buf = red + (t & 1) * (WPH * RED);
+            float* mine = buf + wave * RED;
+            *reinterpret_cast<f32x4*>(mine + col0) = f32x4{u0, u1, u2, u3};
+            *reinterpret_cast<f32x4*>(mine + DV + col0) = f32x4{p0, p1, p2, p3};
+            mine[2 * DV] = kq;
+            lds_barrier();
+            f32x4 ut = *reinterpret_cast<const f32x4*>(buf + col0);
+            f32x4 pt = *reinterpret_cast<const f32x4*>(buf + DV + col0);
+            float kqt = buf[2 * DV];
+#pragma unroll
+            for (int w = 1; w < WPH; ++w) {
+                ut += *reinterpret_cast<const f32x4*>(buf + w * RED + col0);
+                pt += *reinterpret_cast<const f32x4*>(buf + w * RED + DV + col0);
+                kqt += buf[w * RED + 2 * DV];
+            }
+            u0 = ut.x; u1 = ut.y; u2 = ut.z; u3 = ut.w;
+            p0 = pt.x; p1 = pt.y; p2 = pt.z; p3 = pt.w;
+            kq = kqt;
+        }
         if constexpr (!KDA) {
             u0 *= a_head; u1 *= a_head; u2 *= a_head; u3 *= a_head;
             p0 *= a_head; p1 *= a_head; p2 *= a_head; p3 *= a_head;
@@ -277,13 +334,15 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         const float w2 = bt * (vv.z - u2);
         const float w3 = bt * (vv.w - u3);
 
-        if (rg == 0) {
-            st4(o + bth * DV + col0,
-                f32x4{fmaf(kq, w0, p0), fmaf(kq, w1, p1), fmaf(kq, w2, p2), fmaf(kq, w3, p3)});
-        }
+        // Every lane of the head holds the bit-identical o for its columns.
+        // Over several tokens all of them store it (the same values to the
+        // same addresses), which keeps the body free of a branch; a single
+        // token stores from the first row sub-group of wavefront 0 only.
+        const f32x4 ov{fmaf(kq, w0, p0), fmaf(kq, w1, p1), fmaf(kq, w2, p2), fmaf(kq, w3, p3)};
+        if (!ONE || (wave == 0 && sub == 0)) st4(o + bth * DV + col0, ov);
 
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
+        for (int i = 0; i < L; ++i) {
             const float a = KDA ? a_row[i] : a_head;
             const float kk = kv[i];
             s[i].x = fmaf(a, s[i].x, kk * w0);
@@ -292,31 +351,41 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
             s[i].w = fmaf(a, s[i].w, kk * w3);
         }
 
-        if (!ONE && t < n_snap) {
-            float* dst = slots + static_cast<size_t>(t + 1) * TILE;
+        if constexpr (SNAP) {
+            const TileIO<DK, DV> out(slots + static_cast<size_t>(t + 1) * TILE);
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * DV + col0, s[i]);
+            for (int i = 0; i < L; ++i) out.store(off0, i, s[i]);
         }
-        if (!ONE) cur = nxt;
+        if constexpr (!ONE) cur = nxt;
+    };
+
+    if constexpr (ONE) {
+        step(0, std::false_type{});
+    } else {
+        int t = 0;
+        for (; t < n_snap; ++t) step(t, std::true_type{});
+        for (; t < n_tok; ++t) step(t, std::false_type{});
     }
 
     if (K == 1) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) store_state(slots + static_cast<size_t>(row0 + i) * DV + col0, s[i]);
+        for (int i = 0; i < L; ++i) TileIO<DK, DV>(slots).store(off0, i, s[i]);
     }
     if (final_state != nullptr) {
-        float* dst = final_state + static_cast<size_t>(bh) * TILE;
+        const TileIO<DK, DV> out(final_state + static_cast<size_t>(bh) * TILE);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) store_state(dst + static_cast<size_t>(row0 + i) * DV + col0, s[i]);
+        for (int i = 0; i < L; ++i) out.store(off0, i, s[i]);
     }
 }
 
 template <int DK, int DV, bool KDA, bool BF16, bool ONE>
 static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
-    constexpr int WPG = waves_per_group<DV, ONE>();
-    constexpr int NB = DV / (kCPW * WPG);
-    const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * NB);
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE>), grid, dim3(WPG * kWave), 0, stream,
+    // Over several tokens a 128 x 128 tile is split four ways: at two
+    // wavefronts per head the prefetched inputs no longer fit in registers.
+    constexpr int WPH = ONE ? GDN_DEC_WPH_ONE
+                            : (DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI);
+    const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH>), grid, dim3(WPH * kWave), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
                        a.n_snap, a.Hqk, a.group, a.tiled);
 }
