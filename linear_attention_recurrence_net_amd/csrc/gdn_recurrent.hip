@@ -14,8 +14,14 @@
 //    row sub-groups; sub-group `sub` holds the L = RW / RS consecutive rows
 //    sub * L .. sub * L + L - 1 of the block.  One load instruction thus
 //    moves RS whole rows of 4 * d_v bytes, and a lane's k and q rows are
-//    contiguous.  (A copy of a 64 MiB state in this order ran 4.5% faster
-//    on the MI355X than in column blocks of 128-byte row pieces.);
+//    contiguous;
+//  * a single-token launch uses two wavefronts per head (32 rows of a
+//    128 x 128 tile per lane) while the grid fits one resident round, four
+//    beyond it; several tokens use four for 128 x 128 tiles, two otherwise.
+//    Measured on the MI355X with in-place copies of a 64 MiB state: column
+//    blocks of 128-byte row pieces 24.6 us, whole rows with four wavefronts
+//    per head 24.1 us, whole rows with two wavefronts per head meeting at a
+//    barrier between their loads and stores 22.5 us;
 //  * the whole row block is loaded before the first token, so every lane
 //    has L independent 128-bit loads in flight;
 //  * the decay is folded into the reductions (k' = a.k, q' = a.q, applied
@@ -219,20 +225,23 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     float* slots = state + static_cast<size_t>(bh) * K * TILE;
     const uint32_t off0 = static_cast<uint32_t>(row0 * DV + col0) * 4u;  // byte offset in a tile
 
-    f32x4 s[L];
-    {
-        const TileIO<DK, DV> in(slots);
-#pragma unroll
-        for (int i = 0; i < L; ++i) s[i] = in.load(off0, i);
-    }
-
     // Raw inputs of one token, as loaded (bf16 stays packed until used).
+    // The first token's are requested before the state rows: the memory
+    // counter is in order, so the row reduction can then start on the first
+    // rows while later ones are still arriving.
     using Raw = TokenRaw<L, KDA, BF16>;
     const int n_tok = ONE ? 1 : T;
     Raw cur;
     if (n_tok > 0)
         cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h,
                  (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, DK, DV);
+
+    f32x4 s[L];
+    {
+        const TileIO<DK, DV> in(slots);
+#pragma unroll
+        for (int i = 0; i < L; ++i) s[i] = in.load(off0, i);
+    }
     // The first token needs the whole row block and its own inputs, so wait
     // for them here.  Without this wait the loop head would see the first
     // token's input registers as still loading on every iteration; the
@@ -378,24 +387,46 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
 }
 
-template <int DK, int DV, bool KDA, bool BF16, bool ONE>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH>
 static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
-    // Over several tokens a 128 x 128 tile is split four ways: at two
-    // wavefronts per head the prefetched inputs no longer fit in registers.
-    constexpr int WPH = ONE ? GDN_DEC_WPH_ONE
-                            : (DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI);
     const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
     hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH>), grid, dim3(WPH * kWave), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
                        a.n_snap, a.Hqk, a.group, a.tiled);
 }
 
+// Heads that one round of the single-token 128 x 128 kernel holds at two
+// wavefronts per head and two wavefronts per SIMD: four per compute unit.
+// Read once per device.
+static long resident_heads() {
+    static long cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+    if (cache[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+            cu = 256;
+        cache[dev] = 4L * cu;
+    }
+    return cache[dev];
+}
+
 template <int DK, int DV, bool KDA, bool BF16>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
-    if (a.T == 1 && a.n_snap == 0)
-        launch_recurrent_shape<DK, DV, KDA, BF16, true>(a, stream);
-    else
-        launch_recurrent_shape<DK, DV, KDA, BF16, false>(a, stream);
+    if (a.T == 1 && a.n_snap == 0) {
+        // Single token: two wavefronts per head while the grid fits one
+        // resident round (64 MiB of 128 x 128 state: 23.7 us against 25.1 us
+        // at four), four beyond it (2048 heads: 48.6 us against 51.5 us).
+        if (DK == 128 && DV == 128 && static_cast<long>(a.B) * a.H > resident_heads())
+            launch_recurrent_shape<DK, DV, KDA, BF16, true, 4>(a, stream);
+        else
+            launch_recurrent_shape<DK, DV, KDA, BF16, true, GDN_DEC_WPH_ONE>(a, stream);
+    } else {
+        // Over several tokens a 128 x 128 tile is split four ways: at two
+        // wavefronts per head the prefetched inputs no longer fit in registers.
+        constexpr int WPH = DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI;
+        launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH>(a, stream);
+    }
     return hipGetLastError();
 }
 

