@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "3e658bacc23f31b1b7c15a3419cffd10e9847bee2381caf68728b647ba445e83",
-    "fetch_kib": 33508.59375,       # median over 62 decode dispatches
-    "write_kib": 66077.375,
+    "sha256": "2931ae5bd00d270f6e10cae686fa765d23bbae7c39875b831a66e8c384e79d18",
+    "fetch_kib": 33268.5,       # median over 62 decode dispatches
+    "write_kib": 66082.0,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
