@@ -91,21 +91,23 @@ struct TileIO {
 };
 
 // The inputs one lane needs for one token: its RPL rows of k and q, its 4
-// columns of v, beta, and the log-gate (one, or RPL for per-row gates).
+// columns of v, beta, and one log-gate: the head's, or for per-row gates the
+// gate of key row `grow`, whose exponential this lane evaluates for the
+// whole wavefront.
 template <int RPL, bool KDA, bool BF16>
 struct TokenRaw {
     static constexpr int KW = BF16 ? RPL / 2 : RPL;  // 32-bit words per k (or q) slice
     uint32_t kw[KW];
     uint32_t qw[KW];
     uint32_t vw[BF16 ? 2 : 4];
-    float g[KDA ? RPL : 1];
+    float g;
     float beta;
 
     // bth indexes the (sequence, token, value head) of v, g, beta; bthq the
     // (sequence, token, q/k head) of q and k.
     __device__ __forceinline__ void load(const void* q, const void* k, const void* v,
                                          const float* gp, const float* bp, size_t bth,
-                                         size_t bthq, int row0, int col0, int DK, int DV) {
+                                         size_t bthq, int row0, int col0, int grow, int DK, int DV) {
         static_assert(KW % 2 == 0, "row slices are loaded 64 or 128 bits at a time");
         const size_t ko = bthq * DK + row0;  // key index row0 of q and k
         const size_t vo = bth * DV + col0;   // value index col0 of v
@@ -137,14 +139,7 @@ struct TokenRaw {
             uint4 a = *reinterpret_cast<const uint4*>(static_cast<const float*>(v) + vo);
             vw[0] = a.x; vw[1] = a.y; vw[2] = a.z; vw[3] = a.w;
         }
-        if constexpr (KDA) {
-            float tmp[RPL];
-            load_vec<RPL, false>(gp, bth * DK + row0, tmp);
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) g[i] = tmp[i];
-        } else {
-            g[0] = gp[bth];
-        }
+        g = KDA ? gp[bth * DK + grow] : gp[bth];
         beta = bp[bth];
     }
 
@@ -218,6 +213,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int bh = blockIdx.x;  // b * H + h
     const int col0 = cg * 4;
     const int row0 = wave * RW + sub * L;
+    const int grow = wave * RW + lane % RW;  // key row whose decay this lane evaluates (KDA)
     const int b = bh / H;
     const int h = bh - b * H;
     const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
@@ -234,7 +230,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     Raw cur;
     if (n_tok > 0)
         cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h,
-                 (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, DK, DV);
+                 (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, grow, DK, DV);
 
     f32x4 s[L];
     {
@@ -251,9 +247,10 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     if (!ONE) __builtin_amdgcn_s_waitcnt(0);
 
     // One token: the folded update of the row block, the readout, and (SNAP)
-    // the store of the new state to slot t + 1.  The body has no branch, so
-    // the wait the compiler places for the prefetched inputs counts exactly
-    // the stores issued after them and leaves those in flight.
+    // the store of the new state to slot t + 1.  Snapshot and plain tokens
+    // run in separate loops, so no snapshot store sits behind a branch and
+    // the wait the compiler places for the prefetched inputs leaves the
+    // previous token's snapshot stores in flight.
     auto step = [&](int t, auto snap_tag) {
         constexpr bool SNAP = decltype(snap_tag)::value;
         const size_t bth = (static_cast<size_t>(b) * T + t) * H + h;
@@ -263,7 +260,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         Raw nxt;
         if constexpr (!ONE) {
             const int dn = t + 1 < n_tok ? 1 : 0;
-            nxt.load(q, k, v, g, beta, bth + dn * H, bthq + dn * Hqk, row0, col0, DK, DV);
+            nxt.load(q, k, v, g, beta, bth + dn * H, bthq + dn * Hqk, row0, col0, grow, DK, DV);
         }
 
         float kv[L], qv[L];
@@ -274,10 +271,15 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         float a_row[KDA ? L : 1];
         float a_head = 1.0f;
         if constexpr (KDA) {
+            // one exponential per key row of the block, then each lane
+            // gathers the decays of its own rows (row r of the block sits in
+            // lane r)
+            const float ae = expf(cur.g);
 #pragma unroll
-            for (int i = 0; i < L; ++i) a_row[i] = expf(cur.g[i]);
+            for (int i = 0; i < L; ++i)
+                a_row[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((sub * L + i) * 4, __float_as_int(ae)));
         } else {
-            a_head = expf(cur.g[0]);
+            a_head = expf(cur.g);
         }
 
         // in-lane partial sums over this lane's rows
@@ -344,11 +346,15 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         const float w3 = bt * (vv.w - u3);
 
         // Every lane of the head holds the bit-identical o for its columns.
-        // Over several tokens all of them store it (the same values to the
-        // same addresses), which keeps the body free of a branch; a single
-        // token stores from the first row sub-group of wavefront 0 only.
+        // Row sub-group 0 of wavefront 0 stores it, except over several
+        // tokens of a tile smaller than 128 x 128, where every lane stores it
+        // (the same values to the same addresses) and the body keeps no
+        // branch.  Measured on the verify workloads (four tokens): 128 x 128
+        // 25.4 us against 25.9 us with every lane storing, 64 x 64 KDA
+        // 14.8 us against 15.0 us with one lane group storing.
+        constexpr bool O_ALL = !ONE && DK * DV < 128 * 128;
         const f32x4 ov{fmaf(kq, w0, p0), fmaf(kq, w1, p1), fmaf(kq, w2, p2), fmaf(kq, w3, p3)};
-        if (!ONE || (wave == 0 && sub == 0)) st4(o + bth * DV + col0, ov);
+        if (O_ALL || (wave == 0 && sub == 0)) st4(o + bth * DV + col0, ov);
 
 #pragma unroll
         for (int i = 0; i < L; ++i) {
@@ -417,10 +423,13 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
         // Single token: two wavefronts per head while the grid fits one
         // resident round (64 MiB of 128 x 128 state: 23.7 us against 25.1 us
         // at four), four beyond it (2048 heads: 48.6 us against 51.5 us).
-        if (DK == 128 && DV == 128 && static_cast<long>(a.B) * a.H > resident_heads())
-            launch_recurrent_shape<DK, DV, KDA, BF16, true, 4>(a, stream);
-        else
-            launch_recurrent_shape<DK, DV, KDA, BF16, true, GDN_DEC_WPH_ONE>(a, stream);
+        if constexpr (DK == 128 && DV == 128) {
+            if (static_cast<long>(a.B) * a.H > resident_heads()) {
+                launch_recurrent_shape<DK, DV, KDA, BF16, true, 4>(a, stream);
+                return hipGetLastError();
+            }
+        }
+        launch_recurrent_shape<DK, DV, KDA, BF16, true, GDN_DEC_WPH_ONE>(a, stream);
     } else {
         // Over several tokens a 128 x 128 tile is split four ways: at two
         // wavefronts per head the prefetched inputs no longer fit in registers.
