@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "2931ae5bd00d270f6e10cae686fa765d23bbae7c39875b831a66e8c384e79d18",
-    "fetch_kib": 33268.5,       # median over 62 decode dispatches
-    "write_kib": 66082.0,
+    "sha256": "8dcf147b36ccdf23480f1d711efb61cdefd86fadb743a110d46abd9aed2e050c",
+    "fetch_kib": 33265.5,       # median over 62 decode dispatches
+    "write_kib": 66085.0,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }

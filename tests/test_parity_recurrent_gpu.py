@@ -272,3 +272,24 @@ def test_large_decode_grid_sampled_heads():
                                     np.asarray(c.state[b:b + 1, h:h + 1], dtype=np.float64))
         assert rel_err(o[b:b + 1, :, h:h + 1], ro) <= TOL, (b, h)
         assert rel_err(s[b:b + 1, h:h + 1], rst[:, :, 0]) <= TOL, (b, h)
+
+
+@pytest.mark.parametrize("gate", ["gda", "kda"])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_beyond_one_resident_round(gate, dt):
+    """A single-token 128 x 128 grid with more heads than one resident round
+    of two-wavefront workgroups holds (four per compute unit) runs four
+    wavefronts per head; both sides of that threshold match the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H, d = 16, 128
+    for heads in (4 * cus, 4 * cus + H):
+        B = heads // H
+        c = gi.make_case(B, 1, H, d, K=1, gate=gate, qkv_dtype=dt, seed=900 + B)
+        d_ = upload(c)
+        s = d_["state"][:, :, 0].contiguous()
+        o = _gdn().gdn_forward(d_["q"], d_["k"], d_["v"], d_["g"], d_["beta"], s)
+        torch.cuda.synchronize()
+        ro, rst, _ = oracle.forward(*oracle_args(c), c.f64("state"), kda=gate == "kda")
+        eo, es = rel_err(o, ro), rel_err(s, rst[:, :, 0])
+        print(B * H, gate, dt, eo, es, flush=True)
+        assert eo <= TOL and es <= TOL, (B * H, eo, es)
