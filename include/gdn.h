@@ -18,8 +18,10 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major array
  *    (last axis contiguous) owned by the caller.  The library keeps no
- *    global state, never synchronises and launches only on `stream` (a
- *    hipStream_t passed as void*; NULL means the default stream).
+ *    global state beyond each device's compute-unit count, read once per
+ *    device to choose a launch shape; it never synchronises and launches
+ *    only on `stream` (a hipStream_t passed as void*; NULL means the
+ *    default stream).
  *  - Layouts: q, k [B,T,H,d_k]; v, o [B,T,H,d_v]; g [B,T,H] (GDA) or
  *    [B,T,H,d_k] (KDA); beta [B,T,H]; state [B,H,K,d_k,d_v] (slot 0 = input).
  *    q/k/v are float32 or bfloat16 (qkv_dtype); g, beta, state and o are
