@@ -890,13 +890,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
                                              0, 0, 0);
 }
 
-// LDS layout of the chain kernel.  A ring of three slots holds, for three
-// consecutive chunks, the operands that arrive as whole rows: the gate block
-// as it is in the workspace, the K and Q images (k_at layout) and the
-// workgroup's V block.  Loader wavefronts fill the slot of chunk n + 2 while
-// the others compute on chunk n.  Operands that one wavefront reads alone
-// and that the workspace holds in fragment order (its T1 or QKm rows) go
-// straight from memory to its registers.
+// LDS layout of the chain kernel.  A ring of slots holds, for consecutive
+// chunks, the operands that arrive as whole rows: the gate block as it is in
+// the workspace and the K and Q images (k_at layout).  Loader wavefronts fill
+// the slot of chunk n + kAhead while the others compute on chunk n.  Operands
+// that one wavefront reads alone (its T1 or QKm rows in fragment order, the
+// state lanes' V values) go straight from memory to its registers.
 // KDA: the K and Q images are the decayed images KG and QG of the
 // workspace (the state update's K^T operand goes from the workspace straight
 // to the state wavefronts' registers).
