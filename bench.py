@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "8dcf147b36ccdf23480f1d711efb61cdefd86fadb743a110d46abd9aed2e050c",
+    "sha256": "fdb8e2c6a1c1fc7f0ec09085203a08c86a7918962608469f292c13ce97e10660",
     "fetch_kib": 33265.5,       # median over 62 decode dispatches
-    "write_kib": 66085.0,
+    "write_kib": 66082.625,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
