@@ -85,14 +85,19 @@ def test_config1_decode_full_size():
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
-def test_verify_and_rollback_full_size(cfg):
+@pytest.mark.parametrize("with_final", [True, False])
+def test_verify_and_rollback_full_size(cfg, with_final):
+    """The verify workloads at full size, with a final state and without one
+    (the launch the benchmark times: then no state after the last token is
+    stored anywhere, and slot 0 must keep the input bit for bit)."""
     c = gi.workload_case(cfg)
     d = upload(c)
-    fin = torch.empty((c.B, c.H, c.d_k, c.d_v), device="cuda")
+    fin = torch.empty((c.B, c.H, c.d_k, c.d_v), device="cuda") if with_final else None
     o = _gdn().gdn_forward_snapshots(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], fin)
     torch.cuda.synchronize()
     st = d["state"]
     rst = _check_against_oracle(c, o, st, fin)
+    assert np.array_equal(bits(st[:, :, 0]), c.state[:, :, 0].view(np.int32))
 
     before = bits(st)
     acc = torch.from_numpy(c.accepted).to("cuda")
