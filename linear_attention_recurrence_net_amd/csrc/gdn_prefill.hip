@@ -424,6 +424,7 @@ __device__ __forceinline__ void solve_store_t1(float (*sA)[kAP], const float* sB
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            if (2 * ks > t) continue;  // above the diagonal: zero, never read
             u32x2 hi[2], lo[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -594,6 +595,7 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         const int r = 16 * rt + lr;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            if (2 * ks > rt) continue;  // above the diagonal: zero, never read
             u32x2 hi[2], lo[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -838,6 +840,7 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
         const int r = 16 * rt + lr;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            if (2 * ks > rt) continue;  // above the diagonal: zero, never read
             u32x2 hi[2], lo[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -1011,10 +1014,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         auto load_t1 = [&](int n) {
             const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks > w) continue;  // T1 is zero there (and not stored)
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
                     t1[ks][hl] = as_bf16x8(buf_ld16(rw, L::kT1F + frag_off(w, ks, hl, lane)));
+            }
         };
         load_t1(0);
         // V at this lane's rows 16 w + 4 grp + j (j = 0..3) and column `col`
@@ -1097,10 +1102,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
             lds_barrier();  // B2: all of R is in LDS
 
-            // W = T1 R for rows 16 w + l%16 (three hi/lo products, split k order)
+            // W = T1 R for rows 16 w + l%16 (three hi/lo products, split k
+            // order; T1 is zero above the diagonal)
             f32x4 W = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks > w) continue;
                 const int c = 32 * ks + 4 * grp;
                 const bf16x8 rh = ld_split(&sR[0][lr][c], &sR[0][lr][c + 16]);
                 const bf16x8 rl = ld_split(&sR[1][lr][c], &sR[1][lr][c + 16]);
