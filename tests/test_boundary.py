@@ -219,3 +219,15 @@ def test_prefill_ex_validation(lib):
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 1, P, P, P, P, P, P, N, P, P, gda_f - 1, None) == ERR_WS
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, P, P, P, P, P, P, N, P, P, kda_f - 1, None) == ERR_WS
     assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, P, N, N, N, 0, None) == OK
+
+
+def test_bench_runs_on_one_gpu_only():
+    """bench.py measures one GPU: any other --gpus value exits with status 2
+    and says so, before it touches a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
