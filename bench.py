@@ -172,6 +172,22 @@ def run_timed(torch, calls, steps, warmup):
     return region_ms, eager_ms
 
 
+def launch_spread(torch, calls, n=100):
+    """Per-launch GPU time of `n` eager launches (rotating over `calls`),
+    each bracketed by its own pair of HIP events on the launch stream.
+    Returns (p10, median, p90) in microseconds."""
+    cur = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(cur.cuda_stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(cur)
+        calls[i % len(calls)](sp)
+        b.record(cur)
+    torch.cuda.synchronize()
+    us = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    return float(np.percentile(us, 10)), float(np.median(us)), float(np.percentile(us, 90))
+
+
 # ----------------------------------------------------------------------------
 # workloads
 # ----------------------------------------------------------------------------
@@ -231,9 +247,10 @@ def bench_decode(torch, lib, steps, warmup):
     sets = _rotating_sets(torch, d, case, with_state_slot0=True)
     calls = [raw_forward_call(lib, case, s, s["state"], s["o"]) for s in sets]
     region_ms, eager_ms = run_timed(torch, calls, steps, warmup)
+    spread = launch_spread(torch, calls)
     nbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, 1, False, True)
     t = _timing(region_ms, eager_ms, steps)
-    res = dict(case=case, n_sets=len(sets), region_ms=region_ms,
+    res = dict(case=case, n_sets=len(sets), region_ms=region_ms, spread_us=spread,
                tokens_per_s=case.B * case.T * steps / (region_ms * 1e-3),
                bytes=nbytes, achieved_gbs=nbytes / (t["us_per_launch"] * 1e-6) / 1e9, **t)
     del sets, calls
@@ -646,6 +663,8 @@ def main():
             "bytes_per_launch": dec["bytes"],
             "us_per_launch": dec["us_per_launch"],
             "eager_us_per_launch": dec["eager_us_per_launch"],
+            # one event pair per eager launch, 100 launches
+            "launch_us_p10_p50_p90": [round(x, 3) for x in dec["spread_us"]],
         },
         "cpu_baseline": cpu,
         "paths": paths,
