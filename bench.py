@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "fdb8e2c6a1c1fc7f0ec09085203a08c86a7918962608469f292c13ce97e10660",
-    "fetch_kib": 33265.5,       # median over 62 decode dispatches
-    "write_kib": 66082.625,
+    "sha256": "700b5c2c5b8a189331f210c12bd78c9c9151f8dd78a7dc12477e60bfcca0ca25",
+    "fetch_kib": 33265.0,       # median over 62 decode dispatches
+    "write_kib": 66084.3125,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }

@@ -39,6 +39,7 @@
 #include "device_common.hpp"
 #include "gdn_internal.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 // Tuning knobs (streaming loads and stores; wavefronts per head for one and
@@ -412,18 +413,21 @@ static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
 
 // Heads that one round of the single-token 128 x 128 kernel holds at two
 // wavefronts per head and two wavefronts per SIMD: four per compute unit.
-// Read once per device.
+// Read once per device (host threads may race to fill an entry; they all
+// store the same value).
 static long resident_heads() {
-    static long cache[64] = {0};
+    static std::atomic<long> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
-    if (cache[dev] == 0) {
+    long heads = cache[dev].load(std::memory_order_relaxed);
+    if (heads == 0) {
         int cu = 0;
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
             cu = 256;
-        cache[dev] = 4L * cu;
+        heads = 4L * cu;
+        cache[dev].store(heads, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return heads;
 }
 
 template <int DK, int DV, bool KDA, bool BF16>
