@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "9786ef13ef6b8899624a828ad2750e1e176e60e4d4e91bbed59ca1b34d3b59fc",
-    "fetch_kib": 33267.5,       # median over 62 decode dispatches
-    "write_kib": 66084.75,
+    "sha256": "b21c99273762e1f25d5ff12504cbe7f859322abeac7945f3a145a5472aed242b",
+    "fetch_kib": 33270.0,       # median over 62 decode dispatches
+    "write_kib": 66083.9375,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }

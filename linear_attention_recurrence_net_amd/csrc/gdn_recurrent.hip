@@ -65,16 +65,18 @@ namespace gdn {
 namespace {
 
 // One head's d_k x d_v state tile, read and written through a buffer
-// resource: each lane keeps one byte offset (that of its first row).  With
-// SOFF the row's distance from it, a compile-time constant, goes in the
-// scalar offset; otherwise the 4 KiB window of the row goes in the scalar
-// offset and the row inside the window in the vector offset.  Flat
-// addressing spent a 64-bit address per row beyond the first 4 KiB.
-// Measured: the single-token decode (B=64 H=16 d=128) runs 23.25 us with
-// SOFF against 23.9 us without; the four-token verify (B=32 H=16) 25.0 us
-// without against 25.8 us with.  Accesses are streaming (non-temporal)
-// unless the tuning knobs say otherwise.
-template <int DK, int DV, bool SOFF>
+// resource: each lane keeps one byte offset (that of its first row).  Stores,
+// and loads with SOFF_LD, pass the row's distance from it (a compile-time
+// constant) in the scalar offset; other loads put the row's 4 KiB window in
+// the scalar offset and the row inside the window in the vector offset.
+// Flat addressing spent a 64-bit address per row beyond the first 4 KiB.
+// Measured: the single-token decode (B=64 H=16 d=128) runs 23.2 us with
+// scalar-offset loads against 23.9 us without; the four-token verify
+// (B=32 H=16) 25.2 us with window loads against 25.8 us with scalar-offset
+// loads, and 25.0 us with scalar-offset snapshot stores against 25.2 us
+// with window stores.  Accesses are streaming (non-temporal) unless the
+// tuning knobs say otherwise.
+template <int DK, int DV, bool SOFF_LD>
 struct TileIO {
     static constexpr int WIN = 1024 / DV;  // rows per 4 KiB window
     static constexpr int CP = 2;           // cache policy: nt
@@ -83,18 +85,15 @@ struct TileIO {
     __device__ __forceinline__ explicit TileIO(float* tile)
         : r(__builtin_amdgcn_make_buffer_rsrc(tile, 0, DK * DV * 4, 0x00020000)) {}
 
-    __device__ __forceinline__ static uint32_t voff(uint32_t off, int i) {
-        return SOFF ? off : off + (i % WIN) * DV * 4;
-    }
-    __device__ __forceinline__ static int soff(int i) { return SOFF ? i * DV * 4 : (i / WIN) * 4096; }
-
     // row i of this lane's block; off = byte offset of the lane's first row
     __device__ __forceinline__ f32x4 load(uint32_t off, int i) const {
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff(off, i), soff(i),
-                                                                               GDN_DEC_NT_LOAD ? CP : 0));
+        const uint32_t vo = SOFF_LD ? off : off + (i % WIN) * DV * 4;
+        const int so = SOFF_LD ? i * DV * 4 : (i / WIN) * 4096;
+        return __builtin_bit_cast(f32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, GDN_DEC_NT_LOAD ? CP : 0));
     }
     __device__ __forceinline__ void store(uint32_t off, int i, f32x4 v) const {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff(off, i), soff(i),
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, i * DV * 4,
                                                GDN_DEC_NT_STORE ? CP : 0);
     }
 };
