@@ -210,6 +210,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     constexpr int RED = 2 * DV + 4;   // one wavefront's partial sums in LDS: u, p, k.q
     constexpr size_t TILE = static_cast<size_t>(DK) * DV;
     static_assert(L >= 4 && L % 4 == 0 && RW % RS == 0 && DK % WPH == 0, "tiling");
+    static_assert(!KDA || RW <= kWave, "KDA: each lane evaluates one key row's decay");
 
     // partial sums of each wavefront, two buffers by token parity
     __shared__ __attribute__((aligned(16))) float red[WPH > 1 ? 2 * WPH * RED : 4];
@@ -437,6 +438,11 @@ static long resident_heads() {
     return heads;
 }
 
+// Wavefronts per head for a requested count: KDA evaluates one key row's decay
+// per lane, so its wavefronts own at most 64 rows each.
+template <int DK, bool KDA>
+constexpr int heads_split(int wph) { return KDA && DK / wph > kWave ? DK / kWave : wph; }
+
 template <int DK, int DV, bool KDA, bool BF16>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
     if (a.T == 1 && a.n_snap == 0) {
@@ -449,11 +455,11 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
                 return hipGetLastError();
             }
         }
-        launch_recurrent_shape<DK, DV, KDA, BF16, true, GDN_DEC_WPH_ONE>(a, stream);
+        launch_recurrent_shape<DK, DV, KDA, BF16, true, heads_split<DK, KDA>(GDN_DEC_WPH_ONE)>(a, stream);
     } else {
         // Over several tokens a 128 x 128 tile is split four ways: at two
         // wavefronts per head the prefetched inputs no longer fit in registers.
-        constexpr int WPH = DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI;
+        constexpr int WPH = heads_split<DK, KDA>(DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI);
         launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH>(a, stream);
     }
     return hipGetLastError();
