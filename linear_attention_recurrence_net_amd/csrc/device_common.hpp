@@ -9,6 +9,7 @@ namespace gdn {
 constexpr int kWave = 64;  // CDNA4 wavefront width (single target: gfx950)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
@@ -112,6 +113,22 @@ __device__ __forceinline__ float add_xor16(float x) {
 
 __device__ __forceinline__ float add_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two butterflies in one swap: the swap exchanges a's upper (odd) lanes with
+// b's lower (even) ones, so the sum holds a's total where a's group sits in
+// the lower half (even 16-lane rows) and b's total in the upper half (odd
+// rows).  No register copy is needed, unlike a swap of a value with itself.
+//   add_xor32_pair: lanes 0..31 <- a over (l, l^32); lanes 32..63 <- b over the same
+//   add_xor16_pair: rows 0 and 2 <- a over (l, l^16); rows 1 and 3 <- b over the same
+__device__ __forceinline__ float add_xor32_pair(float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float add_xor16_pair(float a, float b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 

@@ -59,6 +59,9 @@
 #ifndef GDN_DEC_WPH_MULTI_128
 #define GDN_DEC_WPH_MULTI_128 4
 #endif
+#ifndef GDN_DEC_DRAFT
+#define GDN_DEC_DRAFT 4  // launches of 1..GDN_DEC_DRAFT tokens load all inputs up front
+#endif
 
 namespace gdn {
 
@@ -193,10 +196,11 @@ __device__ __forceinline__ float sum_subgroups(float x) {
 
 // ONE: the launch has exactly one token and no snapshot (plain decode).
 // DK and DV: key and value head sizes (state rows and columns).  WPH:
-// wavefronts per head, one workgroup per head.  Two wavefronts per SIMD are
+// wavefronts per head, one workgroup per head.  TB > 0: the launch has 1..TB
+// tokens, whose inputs are all loaded before the first token is computed.  Two wavefronts per SIMD are
 // requested (at most 256 registers), so a 1024-head decode grid of 2048
 // wavefronts is resident at once.
-template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB>
 __global__ void __launch_bounds__((WPH * kWave)) __attribute__((amdgpu_waves_per_eu(2)))
 recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const float* __restrict__ g,
@@ -236,10 +240,20 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     // rows while later ones are still arriving.
     using Raw = TokenRaw<L, KDA, BF16>;
     const int n_tok = ONE ? 1 : T;
+    auto load_token = [&](Raw& r, int t) {
+        r.load(q, k, v, g, beta, (static_cast<size_t>(b) * T + t) * H + h,
+               (static_cast<size_t>(b) * T + t) * Hqk + hq, row0, col0, grow, DK, DV);
+    };
     Raw cur;
-    if (n_tok > 0)
-        cur.load(q, k, v, g, beta, (static_cast<size_t>(b) * T) * H + h,
-                 (static_cast<size_t>(b) * T) * Hqk + hq, row0, col0, grow, DK, DV);
+    Raw all[TB > 0 ? TB : 1];
+    if constexpr (TB > 0) {
+        // every token's inputs now (a short draft): no token then waits for a
+        // load issued behind an earlier token's snapshot stores
+#pragma unroll
+        for (int j = 0; j < TB; ++j) load_token(all[j], j < n_tok ? j : n_tok - 1);
+    } else if (n_tok > 0) {
+        load_token(cur, 0);
+    }
 
     f32x4 s[L];
     {
@@ -256,22 +270,16 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     if (!ONE) __builtin_amdgcn_s_waitcnt(0);
     const bool keep_last = K == 1 || final_state != nullptr;
 
-    // One token: the folded update of the row block, the readout, and (SNAP)
-    // the store of the new state to slot t + 1.  Snapshot and plain tokens
-    // run in separate loops, so no snapshot store sits behind a branch and
-    // the wait the compiler places for the prefetched inputs leaves the
+    // One token from its inputs `cur`: the folded update of the row block,
+    // the readout, and the store of the new state to slot t + 1 (SNAP 1:
+    // always, 2: if t < n_snap).  In the streaming form snapshot and plain
+    // tokens run in separate loops, so no snapshot store sits behind a branch
+    // and the wait the compiler places for the prefetched inputs leaves the
     // previous token's snapshot stores in flight.
-    auto step = [&](int t, auto snap_tag) {
-        constexpr bool SNAP = decltype(snap_tag)::value;
+    auto step = [&](int t, const Raw& cur, auto snap_tag) {
+        constexpr int SNAP = decltype(snap_tag)::value;
+        const bool snap = SNAP == 1 || (SNAP == 2 && t < n_snap);
         const size_t bth = (static_cast<size_t>(b) * T + t) * H + h;
-        const size_t bthq = (static_cast<size_t>(b) * T + t) * Hqk + hq;
-        // prefetch the next token while this one is computed (the last token
-        // reloads itself, so the load needs no branch)
-        Raw nxt;
-        if constexpr (!ONE) {
-            const int dn = t + 1 < n_tok ? 1 : 0;
-            nxt.load(q, k, v, g, beta, bth + dn * H, bthq + dn * Hqk, row0, col0, grow, DK, DV);
-        }
 
         float kv[L], qv[L];
         cur.unpack_kq(kv, qv);
@@ -313,23 +321,42 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
             p2 = fmaf(s[i].z, qq, p2);
             p3 = fmaf(s[i].w, qq, p3);
         }
-        // across the row sub-groups of the wavefront
-        u0 = sum_subgroups<CG>(u0);
-        u1 = sum_subgroups<CG>(u1);
-        u2 = sum_subgroups<CG>(u2);
-        u3 = sum_subgroups<CG>(u3);
-        p0 = sum_subgroups<CG>(p0);
-        p1 = sum_subgroups<CG>(p1);
-        p2 = sum_subgroups<CG>(p2);
-        p3 = sum_subgroups<CG>(p3);
+        // across the row sub-groups of the wavefront, then across the
+        // wavefronts of the head through LDS: each wavefront writes its
+        // partials and every lane sums those of its own columns in order
+        // 0..WPH-1.  With 64 columns (four row sub-groups) paired butterflies
+        // finish two sums per swap and leave each lane with two adjacent
+        // column totals of u or p, which it writes; otherwise every lane
+        // holds its sub-group's totals of all four columns and writes those.
+        // Measured on the 64 x 64 KDA verify (B=32 H=32 T=4 K=4): 14.0 us
+        // against 14.6 us; with 128 columns the paired form was neutral on
+        // the verify and 1.1 us slower on the decode.
+        constexpr bool PAIRED = WPH > 1 && CG == 16;
         kq = sum_subgroups<CG>(kq);
-        // across the wavefronts of the head: every lane writes its (equal)
-        // sub-group totals, then sums the wavefronts' partials in order 0..WPH-1
+        if constexpr (!PAIRED) {
+            u0 = sum_subgroups<CG>(u0);
+            u1 = sum_subgroups<CG>(u1);
+            u2 = sum_subgroups<CG>(u2);
+            u3 = sum_subgroups<CG>(u3);
+            p0 = sum_subgroups<CG>(p0);
+            p1 = sum_subgroups<CG>(p1);
+            p2 = sum_subgroups<CG>(p2);
+            p3 = sum_subgroups<CG>(p3);
+        }
         if constexpr (WPH > 1) {
             float* buf = red + (t & 1) * (WPH * RED);
             float* mine = buf + wave * RED;
-            *reinterpret_cast<f32x4*>(mine + col0) = f32x4{u0, u1, u2, u3};
-            *reinterpret_cast<f32x4*>(mine + DV + col0) = f32x4{p0, p1, p2, p3};
+            if constexpr (PAIRED) {
+                // sub 0, 1 | 2, 3 -> u0 u1 p0 p1 | u2 u3 p2 p3, then
+                // sub 0 | 1 | 2 | 3 -> u0 u1 | p0 p1 | u2 u3 | p2 p3
+                const float ra = add_xor32_pair(u0, u2), rb = add_xor32_pair(u1, u3);
+                const float rc = add_xor32_pair(p0, p2), rd = add_xor32_pair(p1, p3);
+                const float x = add_xor16_pair(ra, rc), y = add_xor16_pair(rb, rd);
+                *reinterpret_cast<f32x2*>(mine + (sub & 1) * DV + col0 + (sub >> 1) * 2) = f32x2{x, y};
+            } else {
+                *reinterpret_cast<f32x4*>(mine + col0) = f32x4{u0, u1, u2, u3};
+                *reinterpret_cast<f32x4*>(mine + DV + col0) = f32x4{p0, p1, p2, p3};
+            }
             mine[2 * DV] = kq;
             lds_barrier();
             f32x4 ut = *reinterpret_cast<const f32x4*>(buf + col0);
@@ -372,7 +399,7 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         // K=4: 25.3 us against 25.6 us); smaller tiles keep the body free of
         // the branch (64 x 64 KDA verify: 14.6 us against 15.2 us with it).
         constexpr bool TRIM = DK * DV == 128 * 128;
-        if (ONE || SNAP || !TRIM || keep_last || t + 1 < n_tok) {
+        if (ONE || snap || !TRIM || keep_last || t + 1 < n_tok) {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 const float a = KDA ? a_row[i] : a_head;
@@ -384,20 +411,38 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
             }
         }
 
-        if constexpr (SNAP) {
+        if (snap) {
             const TileIO<DK, DV, ONE> out(slots + static_cast<size_t>(t + 1) * TILE);
 #pragma unroll
             for (int i = 0; i < L; ++i) out.store(off0, i, s[i]);
         }
-        if constexpr (!ONE) cur = nxt;
     };
+    using Plain = std::integral_constant<int, 0>;
+    using Snap = std::integral_constant<int, 1>;
+    using SnapIf = std::integral_constant<int, 2>;
 
     if constexpr (ONE) {
-        step(0, std::false_type{});
+        step(0, cur, Plain{});
+    } else if constexpr (TB > 0) {
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+            if (j < n_tok) step(j, all[j], SnapIf{});
     } else {
+        // prefetch the next token while this one is computed (the last token
+        // reloads itself, so the load needs no branch)
         int t = 0;
-        for (; t < n_snap; ++t) step(t, std::true_type{});
-        for (; t < n_tok; ++t) step(t, std::false_type{});
+        for (; t < n_snap; ++t) {
+            Raw nxt;
+            load_token(nxt, t + 1 < n_tok ? t + 1 : t);
+            step(t, cur, Snap{});
+            cur = nxt;
+        }
+        for (; t < n_tok; ++t) {
+            Raw nxt;
+            load_token(nxt, t + 1 < n_tok ? t + 1 : t);
+            step(t, cur, Plain{});
+            cur = nxt;
+        }
     }
 
     if (K == 1) {
@@ -411,10 +456,10 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
 }
 
-template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB = 0>
 static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH>), grid, dim3(WPH * kWave), 0, stream,
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH, TB>), grid, dim3(WPH * kWave), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
                        a.n_snap, a.Hqk, a.group, a.tiled);
 }
@@ -460,7 +505,14 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
         // Over several tokens a 128 x 128 tile is split four ways: at two
         // wavefronts per head the prefetched inputs no longer fit in registers.
         constexpr int WPH = heads_split<DK, KDA>(DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI);
-        launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH>(a, stream);
+        // Short drafts of a 128 x 128 tile load all their inputs up front
+        // (verify B=32 H=16 T=4 K=4: 25.0 us against 25.2 us streamed); the
+        // 64 x 64 KDA verify measured 0.3-0.6 us slower that way.
+        constexpr bool DRAFT = DK == 128 && DV == 128;
+        if (DRAFT && a.T >= 1 && a.T <= GDN_DEC_DRAFT)
+            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, DRAFT ? GDN_DEC_DRAFT : 0>(a, stream);
+        else
+            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH>(a, stream);
     }
     return hipGetLastError();
 }
