@@ -400,14 +400,18 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         // the branch (64 x 64 KDA verify: 14.6 us against 15.2 us with it).
         constexpr bool TRIM = DK * DV == 128 * 128;
         if (ONE || snap || !TRIM || keep_last || t + 1 < n_tok) {
+            // decay in place, then fuse the rank-1 term into it: each element
+            // stays in its register (fusing the decay into a separate k*w
+            // product made the compiler copy every element back, one extra
+            // instruction per element and token)
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 const float a = KDA ? a_row[i] : a_head;
                 const float kk = kv[i];
-                s[i].x = fmaf(a, s[i].x, kk * w0);
-                s[i].y = fmaf(a, s[i].y, kk * w1);
-                s[i].z = fmaf(a, s[i].z, kk * w2);
-                s[i].w = fmaf(a, s[i].w, kk * w3);
+                s[i].x = fmaf(kk, w0, a * s[i].x);
+                s[i].y = fmaf(kk, w1, a * s[i].y);
+                s[i].z = fmaf(kk, w2, a * s[i].z);
+                s[i].w = fmaf(kk, w3, a * s[i].w);
             }
         }
 
