@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "b21c99273762e1f25d5ff12504cbe7f859322abeac7945f3a145a5472aed242b",
-    "fetch_kib": 33270.0,       # median over 62 decode dispatches
-    "write_kib": 66083.9375,
+    "sha256": "3b4b05005b5d5e8f94d189f05e9d8049ed26b6ea2ec1352fdd716efa22f5077d",
+    "fetch_kib": 33263.5,       # median over 62 decode dispatches
+    "write_kib": 66087.0,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
