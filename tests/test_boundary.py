@@ -231,3 +231,28 @@ def test_bench_runs_on_one_gpu_only():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_bench_traffic_tied_to_kernel_sources(monkeypatch):
+    """bench.py reports the counter-measured decode traffic only for the
+    kernel sources it was measured on; for those it is the calibrated
+    FETCH_SIZE + WRITE_SIZE, close to the algorithmic bytes of the launch."""
+    import hashlib
+    import importlib
+    import sys
+    sys.path.insert(0, ROOT)
+    bench = importlib.import_module("bench")
+    t = dict(bench.DECODE_TRAFFIC)
+    h = hashlib.sha256()
+    for rel in t["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    monkeypatch.setitem(bench.DECODE_TRAFFIC, "sha256", "0" * 64)
+    assert bench.decode_traffic_bytes() is None
+    monkeypatch.setitem(bench.DECODE_TRAFFIC, "sha256", h.hexdigest())
+    got = bench.decode_traffic_bytes()
+    copy = 64 * 1024 * 1024
+    want = t["fetch_kib"] / t["copy_fetch_kib"] * copy + t["write_kib"] / t["copy_write_kib"] * copy
+    assert got == pytest.approx(want, rel=1e-12)
+    algorithmic = bench.recurrent_bytes(64, 1, 16, 128, 1, False, True)
+    assert 0.9 < got / algorithmic < 1.3
