@@ -43,7 +43,7 @@
 #include <type_traits>
 
 // Tuning knobs (streaming loads and stores; wavefronts per head for one and
-// for several tokens).
+// for several tokens; the longest draft whose inputs are loaded up front).
 #ifndef GDN_DEC_NT_LOAD
 #define GDN_DEC_NT_LOAD 1
 #endif
@@ -60,7 +60,7 @@
 #define GDN_DEC_WPH_MULTI_128 4
 #endif
 #ifndef GDN_DEC_DRAFT
-#define GDN_DEC_DRAFT 4  // launches of 1..GDN_DEC_DRAFT tokens load all inputs up front
+#define GDN_DEC_DRAFT 4  // 128 x 128 launches of 1..GDN_DEC_DRAFT tokens load all inputs up front
 #endif
 
 namespace gdn {
