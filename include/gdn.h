@@ -225,10 +225,10 @@ int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,
  * the gate kinds and "llama : enable chunked fused GDN path" for the chunked
  * path).  Arguments as in gdn_prefill_chunked_qk_broadcast, except
  * g [B,T,H,d_k] float32 log-gates and the workspace size, which comes from
- * gdn_prefill_kda_workspace_size.  Within the prefill tolerance of the token
- * recurrence while, on every key row, the log-gates of any 8 consecutive
- * tokens sum to more than -80 (per-token decays stronger than that belong to
- * gdn_forward_qk_broadcast, which has no such limit).
+ * gdn_prefill_kda_workspace_size.  Every log-gate g <= 0 (each decay at most
+ * 1) is in range, however strong: within the prefill tolerance of the token
+ * recurrence.  Chunks in which a key row decays by more than e^-40 across 16
+ * tokens take a slower exact path for their 16 x 16 diagonal blocks.
  */
 size_t gdn_prefill_kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                       int32_t chunk);
@@ -246,8 +246,8 @@ int gdn_prefill_chunked_kda(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32
  *   the MFMA products (round to nearest even), so that the result is the
  *   bf16 path's on the rounded inputs and within the prefill tolerance of
  *   the token recurrence on the float32 inputs.
- * gate: GDN_GATE_HEAD (g [B,T,H]) or GDN_GATE_KEY (g [B,T,H,d_k], the range
- *   stated for gdn_prefill_chunked_kda).
+ * gate: GDN_GATE_HEAD (g [B,T,H]) or GDN_GATE_KEY (g [B,T,H,d_k], log-gates
+ *   g <= 0 as for gdn_prefill_chunked_kda).
  * K, state, final_state: as in gdn_prefill_chunked_snapshots; KDA takes
  *   K == 1 only (GDN_ERR_UNSUPPORTED otherwise).
  * q, k [B,T,H_qk,d_k] and head_map as in gdn_prefill_chunked_qk_broadcast;

@@ -630,13 +630,19 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
 // prep, KDA: the per-key-row decays enter A and QKm inside the sum over keys,
 //   A[r][s]   = beta_r sum_i k_r[i] k_s[i] exp(G_r[i] - G_s[i])   (s < r)
 //   QKm[r][s] =        sum_i q_r[i] k_s[i] exp(G_r[i] - G_s[i])   (s <= r)
-// Each factor exp(G_r - G_s) is split at a reference row m between the
-// rows, exp(G_r - G_m) exp(G_m - G_s), and the two halves scale the MFMA
-// operands: row tile mt (rows 16 mt..) uses m = 16 mt + 8 against every
-// column tile.  For columns of earlier tiles both halves are at most 1; on
-// the diagonal tile each half spans at most 8 tokens of decay, so the
-// operands stay in range while the log-gates of 8 consecutive tokens sum to
-// more than -80 on every key row.  The walk over the key axis goes in steps
+// Each factor exp(G_r - G_s) is split at a reference row m, exp(G_r - G_m)
+// exp(G_m - G_s), and the two halves scale the MFMA operands: row tile mt
+// (rows 16 mt..) takes its first row m = 16 mt against every column tile.
+// With decays of at most 1 (g <= 0) the row half is then at most 1, and so is
+// the column half for every earlier column tile (s < m <= r): those products
+// are safe for any gates, and a half that underflows belongs to a product
+// that is itself below e^-87.  On the diagonal tile the column half
+// exp(G_m - G_s) grows with s; while no key decays by more than e^-40 across
+// the tile, it stays below e^40 and the factorised product is used.
+// Otherwise the tile is formed again after the key walk, one entry at a time
+// in fp32 with each entry's own decay exp(G_r - G_s) <= 1 (exact_diag_tile),
+// and those entries replace the factorised ones, so the path is correct for
+// every g <= 0.  The walk over the key axis goes in steps
 // of 32 keys, so that only 32 of the DK gates per row are live at a time:
 // the cumulative gates G of the step are an inclusive scan over the chunk's
 // rows (16 lanes hold 16 rows; the totals of earlier row tiles are added).
@@ -661,6 +667,69 @@ __device__ __forceinline__ float scan16(float x) {
 // Eight floats -> one bf16 MFMA operand (round to nearest even).
 __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
     return as_bf16x8(u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])});
+}
+
+// bf16 element j of 8 packed in a u32x4.
+__device__ __forceinline__ float bf16_elem(const u32x4& w, int j) {
+    return __uint_as_float((j & 1) ? (w[j >> 1] & 0xffff0000u) : (w[j >> 1] << 16));
+}
+
+// Smallest decay, e^-40, that one key may take across a row tile while its
+// diagonal tile still uses the factorised product (column halves below e^40).
+constexpr float kExactMin = 4.248354255291589e-18f;
+// Diagonal tile mt of A and QKm over keys 32 ks .. 32 ks + 31, one entry at a
+// time in fp32 with each entry's exact decay exp(G_r - G_s) <= 1.  Lane
+// (lr, grp) holds row 16 mt + lr at keys 32 ks + 8 grp + 0..7 and takes the
+// other rows' keys from the lanes of its 16-lane row.  It adds, over its
+// eight keys, P[s] = sum k_r k_s exp(-|G_r - G_s|) and Q[s] = sum q_r k_s
+// exp(-|G_r - G_s|) for r = 16 mt + lr and every row s = 16 mt + 0..15 of the
+// tile: P[s] is A[max(r,s)][min(r,s)] / beta and, for s <= r, Q[s] is
+// QKm[r][s] (with g <= 0 the row further down has the smaller G).  Only
+// differences of G inside the tile enter, so the gates are summed from the
+// tile's first row.  The inputs are read again (they are in L2).
+template <int DK, bool F32>
+__device__ __forceinline__ void exact_diag_tile(const void* q, const void* k, const float* g, int t0,
+                                                int nvalid, int H, int h, int Hqk, int hq, int mt,
+                                                int ks, float (&P)[16], float (&Q)[16], int lane) {
+    const int lr = lane & 15, grp = lane >> 4;
+    const int r = 16 * mt + lr;
+    const int d0 = 32 * ks + 8 * grp;
+    float gl[8], kk[8], qv[8];
+    if (r < nvalid) {
+        const size_t tok = static_cast<size_t>(t0) + r;
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * DK + d0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * DK + d0 + 4);
+        const u32x4 kb = __builtin_bit_cast(u32x4, ld8_in<F32>(k, (tok * Hqk + hq) * DK + d0));
+        const u32x4 qb = __builtin_bit_cast(u32x4, ld8_in<F32>(q, (tok * Hqk + hq) * DK + d0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gl[j] = g0[j];
+            gl[4 + j] = g1[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            kk[j] = bf16_elem(kb, j);
+            qv[j] = bf16_elem(qb, j);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gl[j] = kk[j] = qv[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gl[j] = scan16(gl[j]);  // cumulative over the tile's rows
+
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const int src = (lane & 48) | s;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float ksj = __shfl(kk[j], src, 64);
+            const float gsj = __shfl(gl[j], src, 64);
+            const float t = ksj * __expf(-fabsf(gl[j] - gsj));
+            P[s] = fmaf(t, kk[j], P[s]);
+            Q[s] = fmaf(t, qv[j], Q[s]);
+        }
+    }
 }
 
 template <int DK, int DV, bool F32>
@@ -706,10 +775,7 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
     // (16 keys x 8 bytes) meet distinct banks
     uint16_t (*sKT)[72] = reinterpret_cast<uint16_t (*)[72]>(&sA[0][0]);
 
-    // bf16 element j of 8 packed in a u32x4
-    auto elem = [](const u32x4& w, int j) {
-        return __uint_as_float((j & 1) ? (w[j >> 1] & 0xffff0000u) : (w[j >> 1] << 16));
-    };
+    uint32_t exact_tiles = 0;  // bit mt: diagonal tile mt is formed by exact_diag_tile
 #pragma unroll 1
     for (int ks = 0; ks < KS; ++ks) {
         // this lane: keys d0 + 0..7 of rows 16 t + lr
@@ -751,32 +817,6 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
         for (int j = 0; j < 8; ++j) GL[j] = __shfl(G[3][j], (lane & 48) | 15, 64);
 
-        // A and QKm contributions of these 32 keys
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            float ref[8], x[8], y[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ref[j] = __shfl(G[mt][j], (lane & 48) | 8, 64);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float e = __expf(G[mt][j] - ref[j]);
-                x[j] = elem(kb[mt], j) * e;
-                y[j] = elem(qb[mt], j) * e;
-            }
-            const bf16x8 a = pack8(x);
-            const bf16x8 qa = pack8(y);
-#pragma unroll
-            for (int nt = 0; nt <= mt; ++nt) {
-                float z[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) z[j] = elem(kb[nt], j) * __expf(ref[j] - G[nt][j]);
-                const bf16x8 b = pack8(z);
-                const int p = mt * (mt + 1) / 2 + nt;
-                accA[p] = mfma(a, b, accA[p]);   // rows 16 mt + 4 grp + .., column 16 nt + lr
-                accQ[p] = mfma(b, qa, accQ[p]);  // transposed: row 16 mt + lr, columns 16 nt + 4 grp + ..
-            }
-        }
-
         // the decayed images for the chain; K o exp(G_last - G) goes through
         // sKT (the key-major transpose of this step's 32 keys) into the state
         // update's operand fragments
@@ -787,9 +827,9 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float eg = __expf(G[t][j]);
-                a[j] = elem(kb[t], j) * eg;
-                b[j] = elem(qb[t], j) * eg;
-                const float dk = elem(kb[t], j) * __expf(GL[j] - G[t][j]);
+                a[j] = bf16_elem(kb[t], j) * eg;
+                b[j] = bf16_elem(qb[t], j) * eg;
+                const float dk = bf16_elem(kb[t], j) * __expf(GL[j] - G[t][j]);
                 sKT[8 * grp + j][16 * t + lr] = static_cast<uint16_t>(cvt2(dk, 0.f) & 0xffffu);
             }
             const size_t off = (static_cast<size_t>(16 * t + lr) * DK + d0) * 2;
@@ -816,6 +856,37 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
             for (int j = 0; j < 8; ++j) el[j] = __expf(GL[j]);
             *reinterpret_cast<f32x4*>(E + kEv + d0) = f32x4{el[0], el[1], el[2], el[3]};
             *reinterpret_cast<f32x4*>(E + kEv + d0 + 4) = f32x4{el[4], el[5], el[6], el[7]};
+        }
+
+        // A and QKm contributions of these 32 keys
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            float ref[8], x[8], y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ref[j] = __shfl(G[mt][j], lane & 48, 64);
+            float emin = 1.f;  // this lane's smallest row half: its decay from the tile's first row
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = __expf(G[mt][j] - ref[j]);
+                emin = fminf(emin, e);
+                x[j] = bf16_elem(kb[mt], j) * e;
+                y[j] = bf16_elem(qb[mt], j) * e;
+            }
+            // beyond the factorised range the diagonal tile's product below
+            // is discarded and the tile is formed by exact_diag_tile
+            exact_tiles |= static_cast<uint32_t>(__any(emin < kExactMin)) << mt;
+            const bf16x8 a = pack8(x);
+            const bf16x8 qa = pack8(y);
+#pragma unroll
+            for (int nt = 0; nt <= mt; ++nt) {
+                float z[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) z[j] = bf16_elem(kb[nt], j) * __expf(ref[j] - G[nt][j]);
+                const bf16x8 b = pack8(z);
+                const int p = mt * (mt + 1) / 2 + nt;
+                accA[p] = mfma(a, b, accA[p]);   // rows 16 mt + 4 grp + .., column 16 nt + lr
+                accQ[p] = mfma(b, qa, accQ[p]);  // transposed: row 16 mt + lr, columns 16 nt + 4 grp + ..
+            }
         }
     }
     __syncthreads();  // sBeta
@@ -861,6 +932,52 @@ prefill_prep_kda_kernel(const void* __restrict__ q, const void* __restrict__ k,
             *reinterpret_cast<u32x4*>(wsb + L::kQKF + frag_off(rt, ks, 1, lane)) =
                 u32x4{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
         }
+    }
+
+    // Diagonal tiles with decays beyond the factorised range: formed anew over
+    // all keys, and written over the entries the factorised products gave.
+    // The lane index is read again here, so that no lane-dependent value of
+    // the key walk stays live through the walk for this rarely taken pass:
+    // the walk needs the whole 256-register budget of two wavefronts per SIMD.
+    const int xl = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+#pragma unroll 1
+    for (int mt = 0; mt < 4; ++mt) {
+        if (!((exact_tiles >> mt) & 1u)) continue;
+        float P[16], Q[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) P[s] = Q[s] = 0.f;
+#pragma unroll 1
+        for (int ks = 0; ks < KS; ++ks) exact_diag_tile<DK, F32>(q, k, g, t0, nvalid, H, h, Hqk, hq, mt, ks, P, Q, xl);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {  // the sums over the four key groups
+            P[s] += __shfl_xor(P[s], 16, 64);
+            P[s] += __shfl_xor(P[s], 32, 64);
+            Q[s] += __shfl_xor(Q[s], 16, 64);
+            Q[s] += __shfl_xor(Q[s], 32, 64);
+        }
+        // this lane's entries in the layouts of the writes above: A rows
+        // 16 mt + 4 xg + j of column 16 mt + xr, QKm row 16 mt + xr, columns
+        // 16 mt + 4 xg + j
+        const int xr = xl & 15, xg = xl >> 4;
+        float pa[4], pq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pa[j] = xg == 0 ? P[j] : xg == 1 ? P[4 + j] : xg == 2 ? P[8 + j] : P[12 + j];
+            pq[j] = xg == 0 ? Q[j] : xg == 1 ? Q[4 + j] : xg == 2 ? Q[8 + j] : Q[12 + j];
+        }
+        const int col = 16 * mt + xr;
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * mt + 4 * xg + j;
+            sA[row][col] = col < row ? sBeta[row] * pa[j] : 0.f;
+            x[j] = 4 * xg + j <= xr ? pq[j] : 0.f;
+        }
+        u32x2 hi, lo;
+        split4(x[0], x[1], x[2], x[3], hi, lo);
+        const int half = (mt & 1) * 8;  // the diagonal tile's half of the split-order fragment
+        *reinterpret_cast<u32x2*>(wsb + L::kQKF + frag_off(mt, mt >> 1, 0, xl) + half) = hi;
+        *reinterpret_cast<u32x2*>(wsb + L::kQKF + frag_off(mt, mt >> 1, 1, xl) + half) = lo;
     }
     __syncthreads();
     solve_store_t1<L>(sA, sBeta, wsb, lane);

@@ -41,16 +41,27 @@ def oracle_args(case: gi.Case):
     return [case.f64(n) for n in ("q", "k", "v", "g", "beta")]
 
 
-def rel_err(gpu, ref) -> float:
-    """max|gpu - ref| / max|ref| over one output tensor."""
+def rel_err(gpu, ref, name: str = "") -> float:
+    """max|gpu - ref| / max|ref| over one output tensor.
+
+    When the environment variable GDN_PARITY_LOG names a file, every
+    comparison is appended to it as one tab-separated line: the running
+    test, the tensor's name (or its shape) and the error, so that a GPU run
+    leaves a record of the headroom under each bar.
+    """
     if isinstance(gpu, torch.Tensor):
         gpu = gpu.detach().double().cpu().numpy()
     ref = np.asarray(ref, dtype=np.float64)
     den = np.abs(ref).max()
     num = np.abs(np.asarray(gpu, dtype=np.float64) - ref).max()
-    if den == 0:
-        return float(num)
-    return float(num / den)
+    err = float(num) if den == 0 else float(num / den)
+    log = os.environ.get("GDN_PARITY_LOG")
+    if log:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+        label = name or "x".join(str(n) for n in ref.shape)
+        with open(log, "a") as f:
+            f.write(f"{test}\t{label}\t{err:.3e}\n")
+    return err
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

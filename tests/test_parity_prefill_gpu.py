@@ -43,7 +43,7 @@ def _prefill(case):
 
 def _check(case, o, s, tol=TOL):
     ro, rst, _ = oracle.forward(*oracle_args(case), case.f64("state"))
-    eo, es = rel_err(o, ro), rel_err(s, rst[:, :, 0])
+    eo, es = rel_err(o, ro, "o"), rel_err(s, rst[:, :, 0], "state")
     print(f"B={case.B} T={case.T} H={case.H} d={case.d_k} o {eo:.3e} state {es:.3e}", flush=True)
     assert eo <= tol and es <= tol, (eo, es)
     return eo, es

@@ -47,14 +47,14 @@ def _run_snapshots(case, want_final=True):
 def _check_against_oracle(case, o, st, fin):
     ro, rst, rfin = oracle.forward(*oracle_args(case), case.f64("state"), kda=case.gate == "kda",
                                    want_final=fin is not None)
-    errs = {"o": rel_err(o, ro)}
+    errs = {"o": rel_err(o, ro, "o")}
     n_written = min(case.T, case.K - 1) if case.K > 1 else 0
     if case.K == 1:
-        errs["state"] = rel_err(st[:, :, 0], rst[:, :, 0])
+        errs["state"] = rel_err(st[:, :, 0], rst[:, :, 0], "state")
     for s in range(1, n_written + 1):
-        errs[f"slot{s}"] = rel_err(st[:, :, s], rst[:, :, s])
+        errs[f"slot{s}"] = rel_err(st[:, :, s], rst[:, :, s], f"slot{s}")
     if fin is not None:
-        errs["final"] = rel_err(fin, rfin)
+        errs["final"] = rel_err(fin, rfin, "final")
     print(case.B, case.T, case.H, case.d_k, case.gate, case.qkv_dtype, errs, flush=True)
     for name, e in errs.items():
         assert e <= TOL, (name, e)
@@ -79,7 +79,7 @@ def test_config1_decode_full_size():
     o = _gdn().gdn_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
     torch.cuda.synchronize()
     ro, rst, _ = oracle.forward(*oracle_args(c), c.f64("state"))
-    eo, es = rel_err(o, ro), rel_err(state, rst[:, :, 0])
+    eo, es = rel_err(o, ro, "o"), rel_err(state, rst[:, :, 0], "state")
     print("decode", eo, es, flush=True)
     assert eo <= TOL and es <= TOL
 
