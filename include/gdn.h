@@ -19,9 +19,10 @@
  *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major array
  *    (last axis contiguous) owned by the caller.  The library keeps no
  *    global state beyond each device's compute-unit count, read once per
- *    device to choose a launch shape; it never synchronises and launches
- *    only on `stream` (a hipStream_t passed as void*; NULL means the
- *    default stream).
+ *    device to choose a launch shape, and the address of each device's
+ *    scratch array for gdn_prefill_chunked_ex_noalloc; it never
+ *    synchronises and launches only on `stream` (a hipStream_t passed as
+ *    void*; NULL means the default stream).
  *  - Layouts: q, k [B,T,H,d_k]; v, o [B,T,H,d_v]; g [B,T,H] (GDA) or
  *    [B,T,H,d_k] (KDA); beta [B,T,H]; state [B,H,K,d_k,d_v] (slot 0 = input).
  *    q/k/v are float32 or bfloat16 (qkv_dtype); g, beta, state and o are
@@ -54,7 +55,9 @@ typedef enum {
                                 does not divide H                               */
     GDN_ERR_UNSUPPORTED = 3, /* d_k or d_v not in {64,128}, bad dtype/gate     */
     GDN_ERR_WORKSPACE = 4,   /* prefill workspace missing or too small          */
-    GDN_ERR_HIP = 5          /* the HIP runtime reported a launch error         */
+    GDN_ERR_HIP = 5,         /* the HIP runtime reported a launch error         */
+    GDN_ERR_SCRATCH = 6      /* the problem needs more than the library's fixed
+                                scratch array (gdn_prefill_chunked_ex_noalloc)  */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype; /* dtype of q, k, v only */
@@ -262,6 +265,33 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
                            int32_t K, const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, float* final_state, float* o,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_prefill_chunked_ex for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results and errors are those of
+ * gdn_prefill_chunked_ex without the workspace, which is instead a fixed
+ * array of GDN_PREFILL_SCRATCH_BYTES in the library's own device memory.
+ * Each device that loads the library holds that array until the process
+ * ends; its address is looked up on the first call on a device (with that
+ * device current).  The call allocates nothing.
+ * A problem whose workspace (gdn_prefill_workspace_size_ex) exceeds
+ * GDN_PREFILL_SCRATCH_BYTES returns GDN_ERR_SCRATCH, and nothing is launched
+ * (256 MiB holds, for example, T = 8192 tokens of 16 heads at d = 128 in
+ * every gate kind and input type).  The results are bit-identical to
+ * gdn_prefill_chunked_ex with a caller workspace.
+ * Every call on one device uses the same array, which keeps the last call's
+ * contents (the kernels write every workspace byte they read, so nothing has
+ * to be cleared): calls that may overlap on one device -- on different
+ * streams, or from different host threads -- race and must be ordered by the
+ * caller.
+ */
+#define GDN_PREFILL_SCRATCH_BYTES (256u * 1024u * 1024u)
+int gdn_prefill_chunked_ex_noalloc(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                                   int32_t d_k, int32_t d_v, int32_t chunk, int32_t qkv_dtype,
+                                   int32_t gate, int32_t K, const void* q, const void* k,
+                                   const void* v, const float* g, const float* beta, float* state,
+                                   float* final_state, float* o, void* stream);
 
 /* Static description of a status code. */
 const char* gdn_status_str(int status);

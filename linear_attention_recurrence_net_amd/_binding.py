@@ -31,6 +31,7 @@ EXPORTED = (
     "gdn_prefill_chunked_kda",
     "gdn_prefill_workspace_size_ex",
     "gdn_prefill_chunked_ex",
+    "gdn_prefill_chunked_ex_noalloc",
     "gdn_status_str",
 )
 
@@ -83,6 +84,8 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_workspace_size_ex.restype = sz
     lib.gdn_prefill_chunked_ex.argtypes = [i32] * 11 + [vp] * 9 + [sz, vp]
     lib.gdn_prefill_chunked_ex.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_ex_noalloc.argtypes = [i32] * 11 + [vp] * 9
+    lib.gdn_prefill_chunked_ex_noalloc.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.restype = ctypes.c_int
     lib.gdn_prefill_varlen_workspace_size.argtypes = [i32] * 6
     lib.gdn_prefill_varlen_workspace_size.restype = sz
@@ -390,13 +393,9 @@ def gdn_prefill_workspace_size_ex(B: int, T: int, H: int, d_k: int, d_v: int, ch
     return int(library().gdn_prefill_workspace_size_ex(B, T, H, d_k, d_v, chunk, qkv_dtype, gate))
 
 
-def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_state=None, o=None,
-                           workspace=None, chunk: int = 64):
-    """The general chunked prefill: q/k/v bfloat16 or float32 (rounded to
-    bf16 for the MFMA products), g [B,T,H] (GDA) or [B,T,H,d_k] (KDA),
-    q/k with H_qk heads (head_map), state [B,H,d_k,d_v] (in place) or
-    [B,H,K,d_k,d_v] (K slots as in gdn_prefill_chunked_snapshots; KDA: K = 1),
-    final_state for K > 1.  Returns o."""
+def _prefill_ex_args(q, k, v, g, beta, state, head_map, final_state, o):
+    """Checks shared by the general prefill entry points; returns the sizes,
+    codes and the output tensor (allocated when o is None)."""
     B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
     hm = _head_map(head_map)
     _dev_tensor("state", state, (torch.float32,), dev)
@@ -415,6 +414,18 @@ def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_st
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     _dev_tensor("o", o, (torch.float32,), dev)
     _shape("o", o, (B, T, H, dv))
+    return B, T, H, Hq, hm, dk, dv, dt, gate, K, o, dev
+
+
+def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_state=None, o=None,
+                           workspace=None, chunk: int = 64):
+    """The general chunked prefill: q/k/v bfloat16 or float32 (rounded to
+    bf16 for the MFMA products), g [B,T,H] (GDA) or [B,T,H,d_k] (KDA),
+    q/k with H_qk heads (head_map), state [B,H,d_k,d_v] (in place) or
+    [B,H,K,d_k,d_v] (K slots as in gdn_prefill_chunked_snapshots; KDA: K = 1),
+    final_state for K > 1.  Returns o."""
+    B, T, H, Hq, hm, dk, dv, dt, gate, K, o, dev = _prefill_ex_args(q, k, v, g, beta, state, head_map,
+                                                                    final_state, o)
     need = gdn_prefill_workspace_size_ex(B, T, H, dk, dv, chunk, dt, gate)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -424,6 +435,22 @@ def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_st
         _ptr(state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
         _stream_ptr(dev))
     _check("gdn_prefill_chunked_ex", st)
+    return o
+
+
+def gdn_prefill_chunked_ex_noalloc(q, k, v, g, beta, state, o, head_map="grouped", final_state=None,
+                                   chunk: int = 64):
+    """gdn_prefill_chunked_ex with the library's fixed scratch array as the
+    workspace (for callers that cannot allocate: o must be supplied, and
+    nothing is allocated here or in the library).  Returns o."""
+    if o is None:
+        raise ValueError("o must be supplied: this entry point allocates nothing")
+    B, T, H, Hq, hm, dk, dv, dt, gate, K, o, dev = _prefill_ex_args(q, k, v, g, beta, state, head_map,
+                                                                    final_state, o)
+    st = library().gdn_prefill_chunked_ex_noalloc(
+        B, T, H, Hq, hm, dk, dv, chunk, dt, gate, K, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(final_state), _ptr(o), _stream_ptr(dev))
+    _check("gdn_prefill_chunked_ex_noalloc", st)
     return o
 
 

@@ -1,6 +1,7 @@
-// gdn_api.hip -- the extern "C" entry points of gdn.h: host-side validation,
-// kernel selection and launch on the caller's stream.  Nothing here
-// allocates, synchronises or keeps state between calls.
+// gdn_api.hip -- the extern "C" entry points of gdn.h (all but the no-alloc
+// prefill, in gdn_noalloc.hip): host-side validation, kernel selection and
+// launch on the caller's stream.  Nothing here allocates, synchronises or
+// keeps state between calls.
 
 #include "gdn.h"
 #include "gdn_internal.hpp"
@@ -292,6 +293,8 @@ const char* gdn_status_str(int status) {
             return "unsupported configuration (head size, dtype, gate mode, chunk or alignment)";
         case GDN_ERR_WORKSPACE: return "prefill workspace missing, misaligned or too small";
         case GDN_ERR_HIP: return "HIP runtime error at launch";
+        case GDN_ERR_SCRATCH:
+            return "prefill workspace exceeds the library's fixed scratch array (GDN_PREFILL_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

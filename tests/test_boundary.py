@@ -5,6 +5,8 @@
   pointers, bad sizes, unsupported head sizes / dtypes / gates / chunk
   sizes, misalignment and a short prefill workspace return their status
   codes without launching (so these calls are safe without a GPU);
+* the allocation-free prefill validates exactly as the general prefill and
+  refuses, before any HIP call, a problem larger than its scratch array;
 * the status strings exist for every code;
 * the Python binding refuses CPU tensors (there is no CPU path).
 """
@@ -21,7 +23,7 @@ from linear_attention_recurrence_net_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH = range(7)
 
 
 def _declared_functions():
@@ -46,7 +48,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.gdn_status_str(s)
     assert b"unknown" in lib.gdn_status_str(99)
 
@@ -219,6 +221,34 @@ def test_prefill_ex_validation(lib):
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 1, P, P, P, P, P, P, N, P, P, gda_f - 1, None) == ERR_WS
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, P, P, P, P, P, P, N, P, P, kda_f - 1, None) == ERR_WS
     assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, P, N, N, N, 0, None) == OK
+
+
+SCRATCH_BYTES = 256 * 1024 * 1024  # GDN_PREFILL_SCRATCH_BYTES in include/gdn.h
+
+
+def test_prefill_ex_noalloc_validation(lib):
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    assert "#define GDN_PREFILL_SCRATCH_BYTES (256u * 1024u * 1024u)" in hdr
+    pn = lib.gdn_prefill_chunked_ex_noalloc
+    # B, T, H, H_qk, map, dk, dv, chunk, dtype, gate, K, q, k, v, g, beta, state, final, o, stream
+    assert pn(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 0, P, P, P, P, P, P, N, P, None) == ERR_SHAPE
+    assert pn(1, 100, 4, 3, 0, 128, 128, 64, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_SHAPE
+    assert pn(1, 100, 4, 4, 0, 128, 128, 64, 5, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
+    assert pn(1, 100, 4, 4, 0, 128, 128, 32, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
+    assert pn(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
+    assert pn(1, 100, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, P, P, P, P, P, N, P, None) == ERR_NULL
+    assert pn(1, 0, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, N, N, N, N, P, N, N, None) == OK
+    assert pn(0, 100, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, N, N, N, N, N, N, N, None) == OK
+    # the largest workspace the scratch array holds, and one chunk more
+    wsz = lib.gdn_prefill_workspace_size_ex
+    for dt, gate in ((1, 0), (0, 0), (1, 1), (0, 1)):
+        assert wsz(1, 8192, 16, 128, 128, 64, dt, gate) <= SCRATCH_BYTES  # the prefill workload fits
+        per_chunk = wsz(1, 64, 1, 128, 128, 64, dt, gate)
+        n = SCRATCH_BYTES // per_chunk  # chunks of one head that fit
+        assert wsz(1, 64 * n, 1, 128, 128, 64, dt, gate) <= SCRATCH_BYTES
+        assert wsz(1, 64 * n + 1, 1, 128, 128, 64, dt, gate) > SCRATCH_BYTES
+        assert pn(1, 64 * n + 1, 1, 1, 0, 128, 128, 64, dt, gate, 1,
+                  P, P, P, P, P, P, N, P, None) == ERR_SCRATCH
 
 
 def test_bench_runs_on_one_gpu_only():
