@@ -340,33 +340,79 @@ def bench_verify(torch, lib, cfg, steps, warmup):
     return out
 
 
+def _nbytes(ts) -> int:
+    return sum(t.numel() * t.element_size() for t in ts)
+
+
+def _prefill_sets(torch, tensors, extra_bytes):
+    """Independent copies of a prefill's device tensors (inputs, state, o and
+    workspace), as many as make up >= 1 GiB, so that no timed launch finds its
+    data in the 256 MB Infinity Cache.  `tensors` maps names to the tensors
+    of one set; `extra_bytes` maps the names of buffers allocated per set
+    (o, workspace) to their sizes in bytes."""
+    per_set = _nbytes(tensors.values()) + sum(extra_bytes.values())
+    n_sets = max(2, -(-ROTATE_BYTES // per_set))
+    sets = []
+    for _ in range(n_sets):
+        ds = {k: v.clone() for k, v in tensors.items()}
+        for k, nb in extra_bytes.items():
+            ds[k] = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        sets.append(ds)
+    return sets, per_set
+
+
+def _prefill_result(name, case, t, nb, fl, ws_bytes, n_sets, per_set):
+    sec = t["us_per_launch"] * 1e-6
+    return dict(
+        workload=name, bytes=nb, flops=fl, tokens_per_s=case.B * case.T / sec,
+        achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
+        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
+        workspace_bytes=int(ws_bytes), rotating_sets=n_sets, bytes_per_set=int(per_set), **t,
+    )
+
+
+def _bench_prefill_leg(torch, lib, case, entry, ws_bytes, steps, warmup):
+    """Time one single-sequence prefill entry point over rotating sets.
+    `entry(s)` returns the argument tuple (without the stream) and the C
+    function for set s."""
+    d = upload_case(torch, case)
+    base = {k: v for k, v in d.items() if k != "state"}
+    base["state"] = d["state"][:, :, 0].contiguous()
+    o_bytes = case.B * case.T * case.H * case.d_v * 4
+    sets, per_set = _prefill_sets(torch, base, {"o": o_bytes, "ws": ws_bytes})
+    del d, base
+
+    def mk(s):
+        fn, args = entry(s)
+
+        def call(stream):
+            st = fn(*args, stream)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+        return call
+    t = _timing(*run_timed(torch, [mk(s) for s in sets], steps, warmup), steps)
+    n_sets = len(sets)
+    del sets
+    torch.cuda.empty_cache()
+    return t, n_sets, per_set
+
+
+def _vp(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def bench_prefill(torch, lib, steps, warmup):
     import gdn_inputs as gi
     case = gi.workload_case(4)
-    d = upload_case(torch, case)
-    st0 = d["state"][:, :, 0].contiguous()
     ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
-    vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    args = (case.B, case.T, case.H, case.d_k, case.d_v, 64, vp(d["q"]), vp(d["k"]), vp(d["v"]),
-            vp(d["g"]), vp(d["beta"]), vp(st0), vp(o), vp(ws), ws_bytes)
 
-    def call(stream):
-        s = lib.gdn_prefill_chunked(*args, stream)
-        if s != 0:
-            raise RuntimeError(f"libgdn status {s}")
-    t = _timing(*run_timed(torch, [call], steps, warmup), steps)
-    sec = t["us_per_launch"] * 1e-6
-    nb = prefill_bytes(case.B, case.T, case.H, case.d_k)
-    fl = prefill_flops(case.B, case.T, case.H, case.d_k)
-    return dict(
-        workload=gi.WORKLOADS[4]["name"], bytes=nb, flops=fl,
-        tokens_per_s=case.B * case.T / sec,
-        achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
-        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
-        workspace_bytes=int(ws_bytes), **t,
-    )
+    def entry(s):
+        return lib.gdn_prefill_chunked, (
+            case.B, case.T, case.H, case.d_k, case.d_v, 64, _vp(s["q"]), _vp(s["k"]), _vp(s["v"]),
+            _vp(s["g"]), _vp(s["beta"]), _vp(s["state"]), _vp(s["o"]), _vp(s["ws"]), ws_bytes)
+    t, n_sets, per_set = _bench_prefill_leg(torch, lib, case, entry, ws_bytes, steps, warmup)
+    return _prefill_result(gi.WORKLOADS[4]["name"], case, t, prefill_bytes(case.B, case.T, case.H, case.d_k),
+                           prefill_flops(case.B, case.T, case.H, case.d_k), ws_bytes, n_sets, per_set)
 
 
 VARLEN_WORKLOAD = dict(name="prefill GDA, 8192 tokens packed as 16 sequences of mixed length "
@@ -386,17 +432,24 @@ def bench_prefill_varlen(torch, lib, steps, warmup):
     g, beta, st = t(vc.g), t(vc.beta), t(vc.state)
     cu = torch.from_numpy(vc.cu_seqlens).to("cuda")
     ws_bytes = lib.gdn_prefill_varlen_workspace_size(vc.N, vc.total, vc.H, vc.d, vc.d, 64)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    o = torch.empty((vc.total, vc.H, vc.d), device="cuda")
-    vp = lambda x: ctypes.c_void_p(x.data_ptr())
-    args = (vc.N, vc.total, vc.H, vc.H, 0, vc.d, vc.d, 64, vp(cu), vp(q), vp(k), vp(v), vp(g),
-            vp(beta), vp(st), vp(o), vp(ws), ws_bytes)
+    sets, per_set = _prefill_sets(torch, dict(q=q, k=k, v=v, g=g, beta=beta, state=st, cu=cu),
+                                  {"o": vc.total * vc.H * vc.d * 4, "ws": ws_bytes})
+    del q, k, v, g, beta, st, cu
 
-    def call(stream):
-        s = lib.gdn_prefill_chunked_varlen(*args, stream)
-        if s != 0:
-            raise RuntimeError(f"libgdn status {s}")
-    tm = _timing(*run_timed(torch, [call], steps, warmup), steps)
+    def mk(s):
+        args = (vc.N, vc.total, vc.H, vc.H, 0, vc.d, vc.d, 64, _vp(s["cu"]), _vp(s["q"]), _vp(s["k"]),
+                _vp(s["v"]), _vp(s["g"]), _vp(s["beta"]), _vp(s["state"]), _vp(s["o"]), _vp(s["ws"]),
+                ws_bytes)
+
+        def call(stream):
+            st_ = lib.gdn_prefill_chunked_varlen(*args, stream)
+            if st_ != 0:
+                raise RuntimeError(f"libgdn status {st_}")
+        return call
+    tm = _timing(*run_timed(torch, [mk(s) for s in sets], steps, warmup), steps)
+    n_sets = len(sets)
+    del sets
+    torch.cuda.empty_cache()
     sec = tm["us_per_launch"] * 1e-6
     # per sequence: tokens as in the single-sequence prefill, plus its own state in and out
     nb = prefill_bytes(1, vc.total, vc.H, vc.d) + (vc.N - 1) * 2 * vc.H * 4 * vc.d * vc.d
@@ -405,7 +458,7 @@ def bench_prefill_varlen(torch, lib, steps, warmup):
                 tokens_per_s=vc.total / sec, achieved_gbs=nb / sec / 1e9,
                 frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS, achieved_tflops=fl / sec / 1e12,
                 frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS, workspace_bytes=int(ws_bytes),
-                **tm)
+                rotating_sets=n_sets, bytes_per_set=int(per_set), **tm)
 
 
 SNAP_WORKLOAD = dict(name="verify of a 16-token draft through the chunked path: GDA B=32 H=16 d=128 "
@@ -422,13 +475,14 @@ def bench_prefill_snapshots(torch, lib, steps, warmup):
     d = upload_case(torch, case)
     sets = _rotating_sets(torch, d, case)
     ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    for s in sets:
+        s["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
 
     def chunked(s):
         args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, case.K, vp(s["q"]),
                 vp(s["k"]), vp(s["v"]), vp(s["g"]), vp(s["beta"]), vp(s["state"]), None, vp(s["o"]),
-                vp(ws), ws_bytes)
+                vp(s["ws"]), ws_bytes)
 
         def call(stream):
             st = lib.gdn_prefill_chunked_snapshots(*args, stream)
@@ -455,84 +509,103 @@ def bench_prefill_f32(torch, lib, steps, warmup):
     to bf16 inside the kernels for the MFMA products)."""
     import gdn_inputs as gi
     case = gi.workload_case(4, qkv_dtype="f32")
-    d = upload_case(torch, case)
-    st0 = d["state"][:, :, 0].contiguous()
     ws_bytes = lib.gdn_prefill_workspace_size_ex(case.B, case.T, case.H, case.d_k, case.d_v, 64, 0, 0)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
-    vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, 0, 0, 1, vp(d["q"]), vp(d["k"]),
-            vp(d["v"]), vp(d["g"]), vp(d["beta"]), vp(st0), None, vp(o), vp(ws), ws_bytes)
 
-    def call(stream):
-        s = lib.gdn_prefill_chunked_ex(*args, stream)
-        if s != 0:
-            raise RuntimeError(f"libgdn status {s}")
-    t = _timing(*run_timed(torch, [call], steps, warmup), steps)
-    sec = t["us_per_launch"] * 1e-6
+    def entry(s):
+        return lib.gdn_prefill_chunked_ex, (
+            case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, 0, 0, 1, _vp(s["q"]), _vp(s["k"]),
+            _vp(s["v"]), _vp(s["g"]), _vp(s["beta"]), _vp(s["state"]), None, _vp(s["o"]), _vp(s["ws"]),
+            ws_bytes)
+    t, n_sets, per_set = _bench_prefill_leg(torch, lib, case, entry, ws_bytes, steps, warmup)
     B, T, H, dd = case.B, case.T, case.H, case.d_k
     nb = B * T * H * (3 * 4 * dd + 8 + 4 * dd) + 2 * B * H * 4 * dd * dd
-    fl = prefill_flops(B, T, H, dd)
-    return dict(
-        workload="prefill GDA B=1 T=8192 H=16 d=128 chunk 64 with float32 q/k/v", bytes=nb, flops=fl,
-        tokens_per_s=B * T / sec, achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
-        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
-        workspace_bytes=int(ws_bytes), **t,
-    )
+    return _prefill_result("prefill GDA B=1 T=8192 H=16 d=128 chunk 64 with float32 q/k/v", case, t, nb,
+                           prefill_flops(B, T, H, dd), ws_bytes, n_sets, per_set)
 
 
 def bench_prefill_kda(torch, lib, steps, warmup):
     """The prefill workload's shape with KDA gates (gdn_prefill_chunked_kda)."""
     import gdn_inputs as gi
     case = gi.workload_case(4, gate="kda")
-    d = upload_case(torch, case)
-    st0 = d["state"][:, :, 0].contiguous()
     ws_bytes = lib.gdn_prefill_kda_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    o = torch.empty((case.B, case.T, case.H, case.d_v), device="cuda")
-    vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, vp(d["q"]), vp(d["k"]),
-            vp(d["v"]), vp(d["g"]), vp(d["beta"]), vp(st0), vp(o), vp(ws), ws_bytes)
 
-    def call(stream):
-        s = lib.gdn_prefill_chunked_kda(*args, stream)
-        if s != 0:
-            raise RuntimeError(f"libgdn status {s}")
-    t = _timing(*run_timed(torch, [call], steps, warmup), steps)
-    sec = t["us_per_launch"] * 1e-6
-    nb = prefill_kda_bytes(case.B, case.T, case.H, case.d_k)
-    fl = prefill_flops(case.B, case.T, case.H, case.d_k)
-    return dict(
-        workload="prefill KDA B=1 T=8192 H=16 d=128 chunk 64 (the prefill workload with one "
-                 "log-gate per key row)", bytes=nb, flops=fl,
-        tokens_per_s=case.B * case.T / sec,
-        achieved_gbs=nb / sec / 1e9, frac_of_hbm_peak=nb / sec / 1e9 / HBM_PEAK_GBS,
-        achieved_tflops=fl / sec / 1e12, frac_of_bf16_peak=fl / sec / 1e12 / BF16_PEAK_TFLOPS,
-        workspace_bytes=int(ws_bytes), **t,
-    )
+    def entry(s):
+        return lib.gdn_prefill_chunked_kda, (
+            case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, _vp(s["q"]), _vp(s["k"]),
+            _vp(s["v"]), _vp(s["g"]), _vp(s["beta"]), _vp(s["state"]), _vp(s["o"]), _vp(s["ws"]), ws_bytes)
+    t, n_sets, per_set = _bench_prefill_leg(torch, lib, case, entry, ws_bytes, steps, warmup)
+    return _prefill_result("prefill KDA B=1 T=8192 H=16 d=128 chunk 64 (the prefill workload with one "
+                           "log-gate per key row)", case, t,
+                           prefill_kda_bytes(case.B, case.T, case.H, case.d_k),
+                           prefill_flops(case.B, case.T, case.H, case.d_k), ws_bytes, n_sets, per_set)
 
 
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores
 # ----------------------------------------------------------------------------
-def cpu_baseline(budget_s: float = 10.0):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_runs(fn, tokens_per_call, run_s, runs=3):
+    """`runs` runs of `fn`, each repeated for at least `run_s` seconds;
+    returns the tokens/s of each run (input generation excluded)."""
+    rates = []
+    for _ in range(runs):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= run_s:
+                break
+        rates.append(tokens_per_call * reps / el)
+    return rates
+
+
+def cpu_baseline(run_s: float = 3.5):
+    """The float64 oracle (plain per-token loop, OpenMP over independent
+    (sequence, head) pairs) on the host cores: the decode workload and the
+    prefill workload, each the median of 3 runs of >= run_s seconds."""
     import gdn_inputs as gi
     import oracle
+    threads = oracle.num_threads()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    # decode: B=64 H=16 d=128 T=1, 1024 independent (sequence, head) pairs
     case = gi.workload_case(1)
     args = [case.f64(n) for n in ("q", "k", "v", "g", "beta")]
     st = case.f64("state")
-    oracle.forward(*args, st)  # load / build
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(*args, st)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    tokens = case.B * case.T * reps
-    return dict(value=tokens / el, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"full decode workload (B=64 H=16 d=128 T=1, fp64 per-token loop) "
-                       f"repeated {reps}x in {el:.1f} s, OpenMP over (sequence, head)")
+    oracle.forward(*args, st)  # load / warm
+    dec = _oracle_runs(lambda: oracle.forward(*args, st), case.B * case.T, run_s)
+    # prefill: B=1 T=8192 H=16 d=128 from a zero state, 16 (sequence, head) pairs
+    pc = gi.workload_case(4)
+    pargs = [pc.f64(n) for n in ("q", "k", "v", "g", "beta")]
+    pst = pc.f64("state")
+    pre = _oracle_runs(lambda: oracle.forward(*pargs, pst), pc.B * pc.T, run_s)
+    busy = min(threads, pc.B * pc.H)
+    return dict(
+        value=float(np.median(dec)), unit="tokens/s", cores=threads, kind="oracle",
+        sample=f"full decode workload (B=64 H=16 d=128 T=1), fp64 per-token loop, OpenMP over the "
+               f"1024 (sequence, head) pairs; median of 3 runs of >= {run_s:.1f} s",
+        runs_tokens_per_s=[round(x, 1) for x in dec],
+        nproc=os.cpu_count(), affinity_cpus=affinity, threads=threads, cpu_model=_cpu_model(),
+        prefill=dict(
+            value=float(np.median(pre)), unit="tokens/s", threads_busy=busy, kind="oracle",
+            sample=f"full prefill workload (B=1 T=8192 H=16 d=128, zero initial state), fp64 per-token "
+                   f"loop; {busy} threads busy, since the workload has only {pc.B * pc.H} independent "
+                   f"(sequence, head) pairs; median of 3 runs of >= {run_s:.1f} s",
+            runs_tokens_per_s=[round(x, 1) for x in pre]),
+    )
 
 
 def main():
@@ -631,6 +704,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline()
+        if "prefill_chunked_gda" in paths:  # the prefill path's own baseline, beside it
+            paths["prefill_chunked_gda"]["cpu_baseline"] = cpu["prefill"]
 
     case = dec["case"]
     line = {
