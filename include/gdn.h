@@ -64,7 +64,11 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype; /* dtype of q, k, v only *
 typedef enum { GDN_GATE_HEAD = 0 /* GDA */, GDN_GATE_KEY = 1 /* KDA */ } gdn_gate;
 
 /*
- * Decode / multi-token forward with a single state slot, in place.
+ * Decode / multi-token forward with a single state slot, in place: the fused
+ * recurrence of the llama.cpp commit log, tag b9752, bullet "metal : add
+ * Metal backend for GGML_OP_GATED_DELTA_NET" (GDA or KDA gates, head sizes
+ * 64 and 128), with the single-slot state that the koboldcpp commit log, tag
+ * v1.113.1, bullet "metal: add GDN partial rollback", keeps for K = 1.
  * state [B,H,d_k,d_v] holds S_0 on entry and S_T on return; o [B,T,H,d_v].
  * Equivalent to gdn_forward_snapshots with K = 1 and final_state = NULL
  * (same kernel, bit-identical results).  T = 0 leaves the state unchanged.

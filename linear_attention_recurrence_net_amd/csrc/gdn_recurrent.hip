@@ -42,30 +42,18 @@
 #include <atomic>
 #include <type_traits>
 
-// Tuning knobs (streaming loads and stores; wavefronts per head for one and
-// for several tokens; the longest draft whose inputs are loaded up front).
-#ifndef GDN_DEC_NT_LOAD
-#define GDN_DEC_NT_LOAD 1
-#endif
-#ifndef GDN_DEC_NT_STORE
-#define GDN_DEC_NT_STORE 1
-#endif
-#ifndef GDN_DEC_WPH_ONE
-#define GDN_DEC_WPH_ONE 2
-#endif
-#ifndef GDN_DEC_WPH_MULTI
-#define GDN_DEC_WPH_MULTI 2
-#endif
-#ifndef GDN_DEC_WPH_MULTI_128
-#define GDN_DEC_WPH_MULTI_128 4
-#endif
-#ifndef GDN_DEC_DRAFT
-#define GDN_DEC_DRAFT 4  // 128 x 128 launches of 1..GDN_DEC_DRAFT tokens load all inputs up front
-#endif
-
 namespace gdn {
 
 namespace {
+
+// Fixed launch choices, each measured on the MI355X (reasons at the launcher
+// and at TileIO):
+constexpr bool kNtLoad = true;    // state loads and stores are non-temporal
+constexpr bool kNtStore = true;
+constexpr int kWphOne = 2;        // wavefronts per head for one token
+constexpr int kWphMulti = 2;      // ... for several tokens, tiles below 128 x 128
+constexpr int kWphMulti128 = 4;   // ... for several tokens, 128 x 128 tiles
+constexpr int kDraft = 4;         // 128 x 128 launches of 1..kDraft tokens load all inputs up front
 
 // One head's d_k x d_v state tile, read and written through a buffer
 // resource: each lane keeps one byte offset (that of its first row).  Stores,
@@ -93,11 +81,11 @@ struct TileIO {
         const uint32_t vo = SOFF_LD ? off : off + (i % WIN) * DV * 4;
         const int so = SOFF_LD ? i * DV * 4 : (i / WIN) * 4096;
         return __builtin_bit_cast(f32x4,
-                                  __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, GDN_DEC_NT_LOAD ? CP : 0));
+                                  __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kNtLoad ? CP : 0));
     }
     __device__ __forceinline__ void store(uint32_t off, int i, f32x4 v) const {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, i * DV * 4,
-                                               GDN_DEC_NT_STORE ? CP : 0);
+                                               kNtStore ? CP : 0);
     }
 };
 
@@ -504,17 +492,17 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
                 return hipGetLastError();
             }
         }
-        launch_recurrent_shape<DK, DV, KDA, BF16, true, heads_split<DK, KDA>(GDN_DEC_WPH_ONE)>(a, stream);
+        launch_recurrent_shape<DK, DV, KDA, BF16, true, heads_split<DK, KDA>(kWphOne)>(a, stream);
     } else {
         // Over several tokens a 128 x 128 tile is split four ways: at two
         // wavefronts per head the prefetched inputs no longer fit in registers.
-        constexpr int WPH = heads_split<DK, KDA>(DK == 128 && DV == 128 ? GDN_DEC_WPH_MULTI_128 : GDN_DEC_WPH_MULTI);
+        constexpr int WPH = heads_split<DK, KDA>(DK == 128 && DV == 128 ? kWphMulti128 : kWphMulti);
         // Short drafts of a 128 x 128 tile load all their inputs up front
         // (verify B=32 H=16 T=4 K=4: 25.0 us against 25.2 us streamed); the
         // 64 x 64 KDA verify measured 0.3-0.6 us slower that way.
         constexpr bool DRAFT = DK == 128 && DV == 128;
-        if (DRAFT && a.T >= 1 && a.T <= GDN_DEC_DRAFT)
-            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, DRAFT ? GDN_DEC_DRAFT : 0>(a, stream);
+        if (DRAFT && a.T >= 1 && a.T <= kDraft)
+            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, DRAFT ? kDraft : 0>(a, stream);
         else
             launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH>(a, stream);
     }
