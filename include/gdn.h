@@ -255,8 +255,9 @@ int gdn_prefill_chunked_kda(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32
  *   the token recurrence on the float32 inputs.
  * gate: GDN_GATE_HEAD (g [B,T,H]) or GDN_GATE_KEY (g [B,T,H,d_k], log-gates
  *   g <= 0 as for gdn_prefill_chunked_kda).
- * K, state, final_state: as in gdn_prefill_chunked_snapshots; KDA takes
- *   K == 1 only (GDN_ERR_UNSUPPORTED otherwise).
+ * K, state, final_state: as in gdn_prefill_chunked_snapshots, for GDA and
+ *   for KDA (slot t then holds the state after t tokens with every key row
+ *   decayed by its own gates; the same gdn_rollback_select applies).
  * q, k [B,T,H_qk,d_k] and head_map as in gdn_prefill_chunked_qk_broadcast;
  * v, o, beta as in gdn_prefill_chunked.  The workspace holds at least
  * gdn_prefill_workspace_size_ex(...) bytes (larger for KDA and for float32

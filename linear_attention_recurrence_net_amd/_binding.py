@@ -422,7 +422,7 @@ def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_st
     """The general chunked prefill: q/k/v bfloat16 or float32 (rounded to
     bf16 for the MFMA products), g [B,T,H] (GDA) or [B,T,H,d_k] (KDA),
     q/k with H_qk heads (head_map), state [B,H,d_k,d_v] (in place) or
-    [B,H,K,d_k,d_v] (K slots as in gdn_prefill_chunked_snapshots; KDA: K = 1),
+    [B,H,K,d_k,d_v] (K slots as in gdn_prefill_chunked_snapshots, GDA or KDA),
     final_state for K > 1.  Returns o."""
     B, T, H, Hq, hm, dk, dv, dt, gate, K, o, dev = _prefill_ex_args(q, k, v, g, beta, state, head_map,
                                                                     final_state, o)

@@ -138,8 +138,6 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
     if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
-    // KDA snapshots would need every token's per-row decay inside the chain
-    if (gate == GDN_GATE_KEY && K > 1) return GDN_ERR_UNSUPPORTED;
     // (KDA reads g in 16-byte pieces; GDA reads it as single floats)
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (gate == GDN_GATE_KEY && !aligned16(g)) ||
         !aligned16(state) || !aligned16(o) || (final_state && !aligned16(final_state)))

@@ -1051,7 +1051,8 @@ __global__ void __launch_bounds__(kChainThreads)
 prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, float* __restrict__ state,
                      float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
-                     int Hqk, int group, bool tiled, int K, float* __restrict__ final_state) {
+                     int Hqk, int group, bool tiled, int K, float* __restrict__ final_state,
+                     const void* __restrict__ k_in, const float* __restrict__ g) {
     using L = WsL<DK, DV, KDA, F32>;
     using M = ChainLds<DK, KDA>;
     // K and Q come from the workspace's images for KDA and for float32
@@ -1289,6 +1290,13 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 }
             }
 
+            // KDA snapshots start from the chunk's start state (below)
+            f32x4 Y[KDA ? SMT : 1];
+            if (KDA && n * kC < nsnap) {
+#pragma unroll
+                for (int mt = 0; mt < SMT; ++mt) Y[mt] = S[mt];
+            }
+
             // S <- exp(G_last) S + K^T W' for this wavefront's state rows
             // (KDA: S[i,:] <- exp(G_last[i]) S[i,:] + KD^T W)
 #pragma unroll
@@ -1305,6 +1313,58 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 for (int mt = 0; mt < SMT; ++mt) {
                     S[mt] = mfma(kt[mt][ks], ph, S[mt]);
                     S[mt] = mfma(kt[mt][ks], pl, S[mt]);
+                }
+            }
+            // (the KDA snapshots run after the update, when its K^T operands
+            // are dead: with them live the leg spilled at d_k = 128)
+            // KDA: each state row decays by its own exp(g_r[i]), and the
+            // chunk's images hold decayed keys, so the token's key values and
+            // log-gates at this lane's state rows come from the inputs,
+            // kSnapBatch tokens at a time (the key values rounded to bf16 as
+            // everywhere on this path).
+            if (KDA && n * kC < nsnap) {
+                constexpr int kSnapBatch = 2;  // four spilled at d_k = 128
+                const int rn = min(kC, nsnap - n * kC);
+                const int hq = qk_head(h, Hqk, group, tiled);
+                for (int r0 = 0; r0 < rn; r0 += kSnapBatch) {
+                    f32x4 kv[kSnapBatch][SMT], ag[kSnapBatch][SMT];
+#pragma unroll
+                    for (int j = 0; j < kSnapBatch; ++j) {
+                        const size_t tok = static_cast<size_t>(start) + n * kC + min(r0 + j, rn - 1);
+#pragma unroll
+                        for (int mt = 0; mt < SMT; ++mt) {
+                            const int i0 = SRW * w + 16 * mt + 4 * grp;
+                            ag[j][mt] = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * DK + i0);
+                            const size_t ke = (tok * Hqk + hq) * DK + i0;
+                            if constexpr (F32) {
+                                const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_in) + ke);
+                                const uint32_t lo = cvt2(x[0], x[1]), hi = cvt2(x[2], x[3]);
+                                kv[j][mt] = f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                                                  __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+                            } else {
+                                const u32x2 x = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(k_in) + ke);
+                                kv[j][mt] = f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                                                  __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < kSnapBatch; ++j) {
+                        const int r = r0 + j;
+                        if (r >= rn) break;
+                        const float wv = __uint_as_float(static_cast<uint32_t>(sW[0][lr][r]) << 16) +
+                                         __uint_as_float(static_cast<uint32_t>(sW[1][lr][r]) << 16);
+                        float* dst = st + static_cast<size_t>(n * kC + r + 1) * DK * DV;
+#pragma unroll
+                        for (int mt = 0; mt < SMT; ++mt) {
+                            const int i0 = SRW * w + 16 * mt + 4 * grp;
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) {
+                                Y[mt][rr] = fmaf(kv[j][mt][rr], wv, __expf(ag[j][mt][rr]) * Y[mt][rr]);
+                                dst[static_cast<size_t>(i0 + rr) * DV + col] = Y[mt][rr];
+                            }
+                        }
+                    }
                 }
             }
             if constexpr (KDA) load_kt(min(n + 1, NC - 1));  // kt is not read again in this chunk
@@ -1518,7 +1578,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((prefill_chain_kernel<DK, DV, KDA, F32>), dim3(bh * (DV / 16)), dim3(kChainThreads), 0,
                        stream, q, k, v, a.state, a.o, ws, geo, a.H, a.Hqk, a.group, a.tiled, a.K,
-                       a.final_state);
+                       a.final_state, a.k, a.g);
     return hipGetLastError();
 }
 

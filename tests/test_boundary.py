@@ -217,7 +217,8 @@ def test_prefill_ex_validation(lib):
     # B, T, H, H_qk, map, dk, dv, chunk, dtype, gate, K, q, k, v, g, beta, state, final, o, ws, ws_bytes, stream
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 0, P, P, P, P, P, P, N, P, P, gda_f, None) == ERR_SHAPE
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 5, 0, 1, P, P, P, P, P, P, N, P, P, gda_f, None) == ERR_UNSUP
-    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, P, P, N, P, P, kda_bf, None) == ERR_UNSUP
+    # KDA with K > 1 snapshot slots is accepted up to the workspace check
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, P, P, N, P, P, kda_bf - 1, None) == ERR_WS
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 1, P, P, P, P, P, P, N, P, P, gda_f - 1, None) == ERR_WS
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, P, P, P, P, P, P, N, P, P, kda_f - 1, None) == ERR_WS
     assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, P, N, N, N, 0, None) == OK
@@ -235,7 +236,7 @@ def test_prefill_ex_noalloc_validation(lib):
     assert pn(1, 100, 4, 3, 0, 128, 128, 64, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_SHAPE
     assert pn(1, 100, 4, 4, 0, 128, 128, 64, 5, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
     assert pn(1, 100, 4, 4, 0, 128, 128, 32, 1, 0, 1, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
-    assert pn(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, P, P, N, P, None) == ERR_UNSUP
+    assert pn(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, N, P, N, P, None) == ERR_NULL
     assert pn(1, 100, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, P, P, P, P, P, N, P, None) == ERR_NULL
     assert pn(1, 0, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, N, N, N, N, P, N, N, None) == OK
     assert pn(0, 100, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, N, N, N, N, N, N, N, None) == OK

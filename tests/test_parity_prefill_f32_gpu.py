@@ -94,8 +94,17 @@ def test_prefill_f32_snapshots():
     assert np.array_equal(bits(st[:, :, 0]), c.state[:, :, 0].view(np.int32))
 
 
-def test_prefill_ex_rejects_kda_snapshots():
-    c = gi.make_case(1, 8, 2, 64, K=3, gate="kda", qkv_dtype="bf16", seed=4)
+def test_prefill_ex_kda_snapshots_float32():
+    """KDA with K snapshot slots and float32 inputs through the general entry
+    point (more shapes in the snapshot tests)."""
+    B, T, H, d, K = 2, 20, 2, 64, 6
+    c = gi.make_case(B, T, H, d, K=K, gate="kda", qkv_dtype="f32", seed=4)
+    c.state[:, :, 1:] = np.float32(np.nan)
     u = upload(c)
-    with pytest.raises(Exception):
-        _run_ex(u, state=u["state"])
+    fin = torch.empty((B, H, d, d), device="cuda")
+    o, st = _run_ex(u, state=u["state"], final=fin)
+    ro, rst, rfin = oracle.forward(*oracle_args(c), c.f64("state"), kda=True, want_final=True)
+    assert rel_err(o, ro) <= TOL and rel_err(fin, rfin) <= TOL
+    for t in range(1, K):
+        assert rel_err(st[:, :, t], rst[:, :, t]) <= TOL
+    assert np.array_equal(bits(st[:, :, 0]), c.state[:, :, 0].view(np.int32))
