@@ -1075,6 +1075,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __shared__ __attribute__((aligned(16))) uint16_t sW[2][16][CLD];    // W hi/lo
     __shared__ __attribute__((aligned(16))) uint16_t sWp[2][16][CLD];   // W' = exp(G_last - G) W hi/lo
     __shared__ __attribute__((aligned(16))) float sO[kC][OLD];           // the chunk's output block
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kStateWaves][16][16];  // V rows of each state wavefront
 
     const int lane = threadIdx.x & 63;
     // the role of a wavefront is uniform across it: keep it in a scalar
@@ -1140,9 +1141,11 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
         };
         load_t1(0);
-        // V at this lane's rows 16 w + 4 grp + j (j = 0..3) and column `col`
-        // of a chunk, bf16 bits in the low half (zero past the sequence end)
-        uint32_t vr[4];
+        // The wavefront's 16 rows of V of a chunk in one 8-byte load per
+        // lane: row 16 w + l/4, columns 4 (l%4) + 0..3 of the column block
+        // (zero past the sequence end).  Staged through sV, a transposing read
+        // gives each lane its rows 16 w + 4 grp + 0..3 at column `col`.
+        u32x2 vr;
         auto load_v = [&](int n) {
             const int r0 = n * kC;
             __amdgpu_buffer_rsrc_t rv;
@@ -1150,17 +1153,16 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             if constexpr (F32) {  // the workspace's bf16 V image
                 rv = ws_rsrc(n);
                 rowb = DV * 2;
-                off0 = L::kVI + col * 2;
+                off0 = L::kVI + cb * 32;
             } else {
                 const int row_b16 = H * DV * 2;
                 rv = make_rsrc(v + (static_cast<size_t>(start + r0) * H + h) * DV,
                                (len - 1 - r0) * row_b16 + DV * 2);
                 rowb = row_b16;
-                off0 = col * 2;
+                off0 = cb * 32;
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                vr[j] = __builtin_amdgcn_raw_buffer_load_b16(rv, off0 + (16 * w + 4 * grp + j) * rowb, 0, 0);
+            vr = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, off0 + 8 * (lane & 3) + (16 * w + (lane >> 2)) * rowb, 0, 0));
         };
         load_v(0);
         bf16x8 kt[SMT][2];
@@ -1210,11 +1212,16 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             // R = V - exp(G) X (KDA: V - X, the decay is inside KG) for this
             // wavefront's rows, hi/lo to LDS
             {
+                // sV[w] is this wavefront's alone: its previous reads came
+                // before these writes in program order
+                uint16_t* const pv = &sV[w][0][0] + 4 * lane;  // row l/4, columns 4 (l%4)..
+                *reinterpret_cast<u32x2*>(pv) = vr;
+                const u32x2 vt = ld_tr(pv);
                 u32x2 rh, rl;
-                split4(__uint_as_float(vr[0] << 16) - eg[0] * X[0],
-                       __uint_as_float(vr[1] << 16) - eg[1] * X[1],
-                       __uint_as_float(vr[2] << 16) - eg[2] * X[2],
-                       __uint_as_float(vr[3] << 16) - eg[3] * X[3], rh, rl);
+                split4(__uint_as_float(vt[0] << 16) - eg[0] * X[0],
+                       __uint_as_float(vt[0] & 0xffff0000u) - eg[1] * X[1],
+                       __uint_as_float(vt[1] << 16) - eg[2] * X[2],
+                       __uint_as_float(vt[1] & 0xffff0000u) - eg[3] * X[3], rh, rl);
                 *reinterpret_cast<u32x2*>(&sR[0][lr][16 * w + 4 * grp]) = rh;
                 *reinterpret_cast<u32x2*>(&sR[1][lr][16 * w + 4 * grp]) = rl;
             }
@@ -1234,7 +1241,7 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 W = mfma(t1[ks][1], rh, W);
             }
             load_t1(min(n + 1, NC - 1));  // t1 is not read again in this chunk
-            load_v(min(n + 1, NC - 1));   // nor vr
+            load_v(min(n + 1, NC - 1));   // nor vr (it is in sV)
             // K^T operands of the state update (d_k rows SRW w + 16 mt + l%16,
             // chunk rows in split order), read while W forms (KDA: loaded
             // during the previous chunk)
@@ -1324,25 +1331,37 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             // everywhere on this path).
             if (KDA && n * kC < nsnap) {
                 constexpr int kSnapBatch = 2;  // four spilled at d_k = 128
+                constexpr int EB = F32 ? 4 : 2;  // bytes per key value
                 const int rn = min(kC, nsnap - n * kC);
                 const int hq = qk_head(h, Hqk, group, tiled);
+                const size_t tok0 = static_cast<size_t>(start) + n * kC;
+                // Buffer views of the chunk's gates and keys and of its
+                // snapshot slots, so that the lane's offsets are 32-bit
+                // (4 grp rows in, column `col`) and the rest is scalar.
+                const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + (tok0 * H + h) * DK, ((rn - 1) * H + 1) * DK * 4);
+                const __amdgpu_buffer_rsrc_t rk =
+                    make_rsrc(static_cast<const char*>(k_in) + (tok0 * Hqk + hq) * DK * EB, ((rn - 1) * Hqk + 1) * DK * EB);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(st + static_cast<size_t>(n * kC + 1) * DK * DV, rn * DK * DV * 4);
                 for (int r0 = 0; r0 < rn; r0 += kSnapBatch) {
                     f32x4 kv[kSnapBatch][SMT], ag[kSnapBatch][SMT];
 #pragma unroll
                     for (int j = 0; j < kSnapBatch; ++j) {
-                        const size_t tok = static_cast<size_t>(start) + n * kC + min(r0 + j, rn - 1);
+                        const int r = min(r0 + j, rn - 1);
 #pragma unroll
                         for (int mt = 0; mt < SMT; ++mt) {
-                            const int i0 = SRW * w + 16 * mt + 4 * grp;
-                            ag[j][mt] = *reinterpret_cast<const f32x4*>(g + (tok * H + h) * DK + i0);
-                            const size_t ke = (tok * Hqk + hq) * DK + i0;
+                            const int i0s = SRW * w + 16 * mt;  // + 4 grp in the lane's offset
+                            ag[j][mt] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, 16 * grp, (r * H * DK + i0s) * 4, 0));
+                            const int ko = (r * Hqk * DK + i0s) * EB;
                             if constexpr (F32) {
-                                const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_in) + ke);
+                                const f32x4 x =
+                                    __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * grp, ko, 0));
                                 const uint32_t lo = cvt2(x[0], x[1]), hi = cvt2(x[2], x[3]);
                                 kv[j][mt] = f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
                                                   __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
                             } else {
-                                const u32x2 x = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(k_in) + ke);
+                                const u32x2 x =
+                                    __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 8 * grp, ko, 0));
                                 kv[j][mt] = f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
                                                   __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
                             }
@@ -1354,14 +1373,15 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                         if (r >= rn) break;
                         const float wv = __uint_as_float(static_cast<uint32_t>(sW[0][lr][r]) << 16) +
                                          __uint_as_float(static_cast<uint32_t>(sW[1][lr][r]) << 16);
-                        float* dst = st + static_cast<size_t>(n * kC + r + 1) * DK * DV;
 #pragma unroll
                         for (int mt = 0; mt < SMT; ++mt) {
-                            const int i0 = SRW * w + 16 * mt + 4 * grp;
 #pragma unroll
                             for (int rr = 0; rr < 4; ++rr) {
                                 Y[mt][rr] = fmaf(kv[j][mt][rr], wv, __expf(ag[j][mt][rr]) * Y[mt][rr]);
-                                dst[static_cast<size_t>(i0 + rr) * DV + col] = Y[mt][rr];
+                                // slot n kC + r + 1, state row SRW w + 16 mt + 4 grp + rr, column col
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    __float_as_uint(Y[mt][rr]), rs, (4 * grp * DV + col) * 4,
+                                    (r * DK * DV + (SRW * w + 16 * mt + rr) * DV) * 4, 0);
                             }
                         }
                     }
@@ -1390,10 +1410,12 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         auto load_q = [&](int n) {
             const __amdgpu_buffer_rsrc_t rw = ws_rsrc(n);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * ks > w) continue;  // QKm is zero there (and not read)
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
                     qk[ks][hl] = as_bf16x8(buf_ld16(rw, L::kQKF + frag_off(w, ks, hl, lane)));
+            }
         };
         load_q(0);
         for (int n = 0; n < NC; ++n) {
@@ -1439,20 +1461,22 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     if (wave < kStateWaves + kOutWaves + kLoadWaves) {
         // ====================== loader wavefronts ==========================
-        // Each loader issues the same number of 1 KiB direct-to-LDS loads per
-        // chunk (kPer, the last one repeated where the count does not
-        // divide), in three parts, one after each barrier.  The loads of
-        // chunk n + kAhead (= 3) go out during chunk n, and before chunk
-        // n + 1's first barrier each loader waits until chunk n + 1's loads are
-        // done: only its 2 kPer newest loads, those of chunks n + 2 and n + 3,
-        // may stay outstanding.  Slot (n + 3) % 4 held chunk n - 1, whose last
-        // reads come before chunk n's first barrier.
+        // Each loader issues its own run of the chunk's 1 KiB direct-to-LDS
+        // loads (kPer of them, the last loader the rest: every load is
+        // issued once), in three parts, one after each barrier.  The loads of chunk
+        // n + kAhead (= 3) go out during chunk n, and before chunk n + 1's
+        // first barrier each loader waits until chunk n + 1's loads are done:
+        // only its loads of chunks n + 2 and n + 3 may stay outstanding.
+        // Slot (n + 3) % 4 held chunk n - 1, whose last reads come before
+        // chunk n's first barrier.
         const int l = wave - kStateWaves - kOutWaves;
         const int hq = qk_head(h, Hqk, group, tiled);  // the q/k head this value head reads
         const size_t headq0 = (static_cast<size_t>(start) * Hqk + hq) * DK;  // q/k element (start, hq, 0)
         const int rowq_b16 = Hqk * DK * 2;                                   // bytes per token of q, k
         const int seqq_b16 = (len - 1) * rowq_b16 + DK * 2;  // end of the last valid row of q, k
         constexpr int kPer = (M::kLoads + kLoadWaves - 1) / kLoadWaves;
+        constexpr int kLast = M::kLoads - kPer * (kLoadWaves - 1);  // loads of the last loader
+        static_assert(kLast > 0 && kLast <= kPer, "every loader has loads");
         // parts of kP01, kP01 and the rest: little is left for after B3, so
         // that a loader reaches B1 (after waiting for the next chunk) early
         constexpr int kP01 = kPer / 2;
@@ -1467,8 +1491,8 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const int j0 = qt * kP01, j1 = qt == 2 ? kPer : (qt + 1) * kP01;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
-                if (j < j0 || j >= j1) continue;
-                const int i = min(kPer * l + j, M::kLoads - 1);
+                const int i = kPer * l + j;
+                if (j < j0 || j >= j1 || i >= M::kLoads) continue;
                 if (i == 0) {
                     dma16(rw, slot + M::kE, L::kE + 16 * lane);
                 } else {
@@ -1500,7 +1524,11 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             lds_barrier();  // B3
             if (more) {
                 load(n + A, 2);
-                vm_wait_keep<(A - 1) * kPer>();  // chunk n + 1's loads are done
+                // chunk n + 1's loads are done
+                if (l < kLoadWaves - 1)
+                    vm_wait_keep<(A - 1) * kPer>();
+                else
+                    vm_wait_keep<(A - 1) * kLast>();
             } else {
                 vm_wait_all();
             }

@@ -18,14 +18,8 @@
 
 namespace gdn {
 
-#ifndef GDN_RB_THREADS
-#define GDN_RB_THREADS 128
-#endif
-#ifndef GDN_RB_BARRIER
-#define GDN_RB_BARRIER 1
-#endif
-
-constexpr int kCopyThreads = GDN_RB_THREADS;
+// Two wavefronts per (sequence, head) tile.
+constexpr int kCopyThreads = 128;
 
 template <int PER_LANE>
 __global__ void __launch_bounds__(kCopyThreads)
@@ -47,10 +41,9 @@ rollback_kernel(const int32_t* __restrict__ accepted, float* __restrict__ state,
         f32x4 r[PER_LANE];
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) r[i] = ld4_nt(src + 4 * (i * kCopyThreads + threadIdx.x));
-#if GDN_RB_BARRIER
+        // every load has landed before any lane of the group stores
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-#endif
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) st4_nt(base + 4 * (i * kCopyThreads + threadIdx.x), r[i]);
     } else {
