@@ -17,6 +17,10 @@ Entry points (same names as the C ABI):
 """
 
 from ._binding import (  # noqa: F401
+    GDN_BF16,
+    GDN_F32,
+    GDN_GATE_HEAD,
+    GDN_GATE_KEY,
     GdnError,
     gdn_forward,
     gdn_forward_qk_broadcast,
