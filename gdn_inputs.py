@@ -206,9 +206,11 @@ def workload_case(i: int, seed: int | None = None, **override) -> Case:
 
 @dataclasses.dataclass
 class VarlenCase:
-    """Sequences of different lengths packed along the token axis (bf16 q/k/v,
-    GDA gates).  q, k [total, H_qk, d]; v [total, H, d]; g, beta [total, H];
-    state [N, H, d, d] (one initial state per sequence); cu_seqlens [N+1]."""
+    """Sequences of different lengths packed along the token axis.  q, k
+    [total, H_qk, d]; v [total, H, d]; g [total, H] (GDA) or [total, H, d]
+    (KDA); beta [total, H]; state [N, H, d, d] (one initial state per
+    sequence); cu_seqlens [N+1]; q/k/v values bf16-representable unless
+    qkv_dtype is "f32"."""
 
     lengths: list
     H: int
@@ -220,6 +222,8 @@ class VarlenCase:
     beta: np.ndarray
     state: np.ndarray
     cu_seqlens: np.ndarray
+    gate: str = "gda"
+    qkv_dtype: str = "bf16"
 
     @property
     def N(self) -> int:
@@ -237,22 +241,23 @@ class VarlenCase:
         """Sequence i alone as a B = 1 case (its rows of the packed arrays)."""
         a, b = int(self.cu_seqlens[i]), int(self.cu_seqlens[i + 1])
         st = self.state[i][None, :, None].copy()
-        return Case(1, b - a, self.H, self.d, self.d, 1, "gda", "bf16", self.q[None, a:b].copy(),
+        return Case(1, b - a, self.H, self.d, self.d, 1, self.gate, self.qkv_dtype, self.q[None, a:b].copy(),
                     self.k[None, a:b].copy(), self.v[None, a:b].copy(), self.g[None, a:b].copy(),
                     self.beta[None, a:b].copy(), st, None)
 
 
-def make_varlen_case(lengths, H: int, d: int, *, H_qk: int | None = None, seed: int = 0) -> VarlenCase:
+def make_varlen_case(lengths, H: int, d: int, *, H_qk: int | None = None, seed: int = 0,
+                     gate: str = "gda", qkv_dtype: str = "bf16") -> VarlenCase:
     """Packed sequences with the recipe of make_case: one make_case draw over
     all tokens (B = 1), cut at the sequence boundaries, and N initial states
     drawn after it from the same generator stream."""
     total = int(sum(lengths))
-    c = make_case(1, total, H, d, seed=seed, H_qk=H_qk)
+    c = make_case(1, total, H, d, seed=seed, H_qk=H_qk, gate=gate, qkv_dtype=qkv_dtype)
     rng = np.random.default_rng(seed + 1)
     s0 = np.ascontiguousarray(rng.normal(0.0, 0.1, size=(len(lengths), H, d, d)), dtype=np.float32)
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
-    return VarlenCase(list(lengths), H, d, c.q[0], c.k[0], c.v[0], c.g[0], c.beta[0], s0, cu)
+    return VarlenCase(list(lengths), H, d, c.q[0], c.k[0], c.v[0], c.g[0], c.beta[0], s0, cu, gate, qkv_dtype)
 
 
 def varlen_lengths(total: int, n: int, seed: int = 0, max_len: int | None = None) -> list:

@@ -272,6 +272,26 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The variable-length prefill of gdn_prefill_chunked_varlen with the gate
+ * kind and input type of gdn_prefill_chunked_ex (the same pages' bullets):
+ * qkv_dtype GDN_BF16 or GDN_F32, gate GDN_GATE_HEAD (g [total_T,H]) or
+ * GDN_GATE_KEY (g [total_T,H,d_k], 16-byte aligned).  Every other argument,
+ * the offsets' clamping and the limits as in gdn_prefill_chunked_varlen;
+ * the workspace holds at least gdn_prefill_varlen_workspace_size_ex(...)
+ * bytes, 256-byte aligned.  Each sequence's result is bit-identical to
+ * gdn_prefill_chunked_ex on that sequence alone (K = 1).
+ */
+size_t gdn_prefill_varlen_workspace_size_ex(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
+                                            int32_t d_v, int32_t chunk, int32_t qkv_dtype,
+                                            int32_t gate);
+int gdn_prefill_chunked_varlen_ex(int32_t N, int32_t total_T, int32_t H, int32_t H_qk,
+                                  int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                  int32_t qkv_dtype, int32_t gate, const int32_t* cu_seqlens,
+                                  const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, float* state, float* o, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * gdn_prefill_chunked_ex for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Arguments, results and errors are those of

@@ -32,6 +32,8 @@ EXPORTED = (
     "gdn_prefill_workspace_size_ex",
     "gdn_prefill_chunked_ex",
     "gdn_prefill_chunked_ex_noalloc",
+    "gdn_prefill_varlen_workspace_size_ex",
+    "gdn_prefill_chunked_varlen_ex",
     "gdn_status_str",
 )
 
@@ -90,6 +92,10 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_varlen_workspace_size.argtypes = [i32] * 6
     lib.gdn_prefill_varlen_workspace_size.restype = sz
     lib.gdn_prefill_chunked_varlen.argtypes = [i32] * 8 + [vp] * 9 + [sz, vp]
+    lib.gdn_prefill_varlen_workspace_size_ex.argtypes = [i32] * 8
+    lib.gdn_prefill_varlen_workspace_size_ex.restype = sz
+    lib.gdn_prefill_chunked_varlen_ex.argtypes = [i32] * 10 + [vp] * 9 + [sz, vp]
+    lib.gdn_prefill_chunked_varlen_ex.restype = ctypes.c_int
     lib.gdn_prefill_chunked_varlen.restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
@@ -459,24 +465,23 @@ def gdn_prefill_varlen_workspace_size(N: int, total_T: int, H: int, d_k: int, d_
     return int(library().gdn_prefill_varlen_workspace_size(N, total_T, H, d_k, d_v, chunk))
 
 
-def gdn_prefill_chunked_varlen(cu_seqlens, q, k, v, g, beta, state, head_map="grouped", o=None,
-                               workspace=None, chunk: int = 64):
-    """Chunked prefill of N packed sequences of different lengths.
+def gdn_prefill_varlen_workspace_size_ex(N: int, total_T: int, H: int, d_k: int, d_v: int,
+                                         chunk: int = 64, qkv_dtype: int = GDN_BF16,
+                                         gate: int = GDN_GATE_HEAD) -> int:
+    return int(library().gdn_prefill_varlen_workspace_size_ex(N, total_T, H, d_k, d_v, chunk, qkv_dtype,
+                                                              gate))
 
-    cu_seqlens: device int32 [N+1] token offsets (sequence i is tokens
-    cu_seqlens[i]:cu_seqlens[i+1]); q, k [total,H_qk,d_k]; v [total,H,d_v];
-    g, beta [total,H]; state [N,H,d_k,d_v] updated in place; returns o
-    [total,H,d_v] (rows outside every sequence are left as allocated).
-    """
-    _dev_tensor("q", q, (torch.bfloat16,))
+
+def _varlen_args(fn, cu_seqlens, q, k, v, g, beta, state, head_map, o, bf16_only):
+    _dev_tensor("q", q, (torch.bfloat16,) if bf16_only else (torch.bfloat16, torch.float32))
     dev = q.device
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k must be [total,H_qk,d_k] and v [total,H,d_v]")
     # reuse the [B,T,H,d] checks with B = 1
     B, T, H, dk, dv, dt, gate, _, Hq = _qkv_gate(q[None], k[None], v[None], g[None], beta[None],
                                                 shared_qk=True)
-    if gate != GDN_GATE_HEAD:
-        raise GdnError("gdn_prefill_chunked_varlen", 3, "chunked prefill supports GDA gates only")
+    if bf16_only and gate != GDN_GATE_HEAD:
+        raise GdnError(fn, 3, "this entry point takes GDA gates; gdn_prefill_chunked_varlen_ex takes both")
     hm = _head_map(head_map)
     _dev_tensor("cu_seqlens", cu_seqlens, (torch.int32,), dev)
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
@@ -488,6 +493,21 @@ def gdn_prefill_chunked_varlen(cu_seqlens, q, k, v, g, beta, state, head_map="gr
         o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     _dev_tensor("o", o, (torch.float32,), dev)
     _shape("o", o, (T, H, dv))
+    return N, T, H, Hq, hm, dk, dv, dt, gate, o, dev
+
+
+def gdn_prefill_chunked_varlen(cu_seqlens, q, k, v, g, beta, state, head_map="grouped", o=None,
+                               workspace=None, chunk: int = 64):
+    """Chunked prefill of N packed sequences of different lengths.
+
+    cu_seqlens: device int32 [N+1] token offsets (sequence i is tokens
+    cu_seqlens[i]:cu_seqlens[i+1]); q, k [total,H_qk,d_k] bfloat16;
+    v [total,H,d_v]; g, beta [total,H]; state [N,H,d_k,d_v] updated in
+    place; returns o [total,H,d_v] (rows outside every sequence are left as
+    allocated).
+    """
+    N, T, H, Hq, hm, dk, dv, dt, gate, o, dev = _varlen_args(
+        "gdn_prefill_chunked_varlen", cu_seqlens, q, k, v, g, beta, state, head_map, o, True)
     need = gdn_prefill_varlen_workspace_size(N, T, H, dk, dv, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -496,4 +516,22 @@ def gdn_prefill_chunked_varlen(cu_seqlens, q, k, v, g, beta, state, head_map="gr
         N, T, H, Hq, hm, dk, dv, chunk, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
         _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check("gdn_prefill_chunked_varlen", st)
+    return o
+
+
+def gdn_prefill_chunked_varlen_ex(cu_seqlens, q, k, v, g, beta, state, head_map="grouped", o=None,
+                                  workspace=None, chunk: int = 64):
+    """gdn_prefill_chunked_varlen with the gate kind and input type of
+    gdn_prefill_chunked_ex: q/k/v bfloat16 or float32, g [total,H] (GDA) or
+    [total,H,d_k] (KDA).  Returns o."""
+    N, T, H, Hq, hm, dk, dv, dt, gate, o, dev = _varlen_args(
+        "gdn_prefill_chunked_varlen_ex", cu_seqlens, q, k, v, g, beta, state, head_map, o, False)
+    need = gdn_prefill_varlen_workspace_size_ex(N, T, H, dk, dv, chunk, dt, gate)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked_varlen_ex(
+        N, T, H, Hq, hm, dk, dv, chunk, dt, gate, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
+    _check("gdn_prefill_chunked_varlen_ex", st)
     return o

@@ -205,17 +205,27 @@ int gdn_prefill_chunked_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_
                                          stream);
 }
 
-size_t gdn_prefill_varlen_workspace_size(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
-                                         int32_t d_v, int32_t chunk) {
+size_t gdn_prefill_varlen_workspace_size_ex(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
+                                            int32_t d_v, int32_t chunk, int32_t qkv_dtype,
+                                            int32_t gate) {
     if (N < 0 || total_T < 0 || H < 0 || chunk != 64 || !supported_head(d_k, d_v)) return 0;
-    return gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v);
+    if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return 0;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return 0;
+    return gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v, gate == GDN_GATE_KEY,
+                                               qkv_dtype == GDN_F32);
 }
 
-int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_qk,
-                               int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
-                               const int32_t* cu_seqlens, const void* q, const void* k,
-                               const void* v, const float* g, const float* beta, float* state,
-                               float* o, void* workspace, size_t workspace_bytes, void* stream) {
+size_t gdn_prefill_varlen_workspace_size(int32_t N, int32_t total_T, int32_t H, int32_t d_k,
+                                         int32_t d_v, int32_t chunk) {
+    return gdn_prefill_varlen_workspace_size_ex(N, total_T, H, d_k, d_v, chunk, GDN_BF16, GDN_GATE_HEAD);
+}
+
+int gdn_prefill_chunked_varlen_ex(int32_t N, int32_t total_T, int32_t H, int32_t H_qk,
+                                  int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                  int32_t qkv_dtype, int32_t gate, const int32_t* cu_seqlens,
+                                  const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, float* state, float* o, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
     if (N < 0 || total_T < 0 || H < 0 || chunk < 1) return GDN_ERR_SHAPE;
     const int hs = validate_heads(H, H_qk, head_map);
     if (hs != GDN_OK) return hs;
@@ -224,13 +234,18 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (N > 0 && H > 0 && !state) return GDN_ERR_NULL;
     if (chunk != 64 || !supported_head(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
+    if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
+    // (KDA reads g in 16-byte pieces; GDA reads it as single floats)
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (gate == GDN_GATE_KEY && !aligned16(g)) ||
+        !aligned16(state) || !aligned16(o))
         return GDN_ERR_UNSUPPORTED;
     if (N == 0 || H == 0 || total_T == 0) return GDN_OK;
     // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
     if (static_cast<int64_t>(total_T) * H * (d_k > d_v ? d_k : d_v) * 4 >= (int64_t(1) << 31))
         return GDN_ERR_UNSUPPORTED;
-    const size_t need = gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v);
+    const bool kda = gate == GDN_GATE_KEY, f32 = qkv_dtype == GDN_F32;
+    const size_t need = gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v, kda, f32);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_WORKSPACE;
@@ -246,8 +261,8 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     a.cu_seqlens = cu_seqlens;
     a.final_state = nullptr;
     a.K = 1;
-    a.kda = false;
-    a.f32 = false;
+    a.kda = kda;
+    a.f32 = f32;
     a.B = N;
     a.T = total_T;
     a.H = H;
@@ -257,6 +272,16 @@ int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;
     return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_prefill_chunked_varlen(int32_t N, int32_t total_T, int32_t H, int32_t H_qk,
+                               int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                               const int32_t* cu_seqlens, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, float* state,
+                               float* o, void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_prefill_chunked_varlen_ex(N, total_T, H, H_qk, head_map, d_k, d_v, chunk, GDN_BF16,
+                                         GDN_GATE_HEAD, cu_seqlens, q, k, v, g, beta, state, o,
+                                         workspace, workspace_bytes, stream);
 }
 
 int gdn_prefill_chunked(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,

@@ -268,9 +268,9 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, bool kda, bo
 
 // Variable lengths: at most total / C + N chunks over all sequences (each
 // sequence adds at most one partial chunk), plus the table.
-size_t prefill_varlen_workspace_bytes(int N, int total, int H, int dk, int dv) {
+size_t prefill_varlen_workspace_bytes(int N, int total, int H, int dk, int dv, bool kda, bool f32) {
     const size_t ct = (static_cast<size_t>(total) + kC - 1) / kC + N;
-    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(dk, dv, false, false);
+    return table_bytes(N) + static_cast<size_t>(H) * ct * block_bytes(dk, dv, kda, f32);
 }
 
 // ---------------------------------------------------------------------------

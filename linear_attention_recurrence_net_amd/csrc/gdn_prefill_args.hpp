@@ -27,7 +27,8 @@ struct PrefillArgs {
 };
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, bool kda = false, bool f32 = false);
-size_t prefill_varlen_workspace_bytes(int N, int total, int H, int dk, int dv);
+size_t prefill_varlen_workspace_bytes(int N, int total, int H, int dk, int dv, bool kda = false,
+                                      bool f32 = false);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

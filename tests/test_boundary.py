@@ -174,6 +174,27 @@ def test_prefill_varlen_validation(lib):
     assert pv(3, 0, 4, 2, 0, 128, 128, 64, P, N, N, N, N, N, P, N, N, 0, None) == OK
 
 
+def test_prefill_varlen_ex_validation(lib):
+    wsz = lib.gdn_prefill_varlen_workspace_size_ex
+    base = wsz(3, 300, 4, 128, 128, 64, 1, 0)
+    assert base == lib.gdn_prefill_varlen_workspace_size(3, 300, 4, 128, 128, 64) > 0
+    kda, f32 = wsz(3, 300, 4, 128, 128, 64, 1, 1), wsz(3, 300, 4, 128, 128, 64, 0, 0)
+    assert kda > base and f32 > base  # decayed images; bf16 images of the float32 rows
+    assert wsz(3, 300, 4, 128, 128, 64, 2, 0) == 0 and wsz(3, 300, 4, 128, 128, 64, 1, 2) == 0
+    pv = lib.gdn_prefill_chunked_varlen_ex
+    # N, total, H, H_qk, map, dk, dv, chunk, dtype, gate, cu, q, k, v, g, beta, state, o, ws, ws_bytes, stream
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, N, P, P, P, P, P, P, P, P, kda, None) == ERR_NULL
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, P, P, P, P, N, P, P, P, P, kda, None) == ERR_NULL
+    assert pv(-1, 300, 4, 2, 0, 128, 128, 64, 1, 1, P, P, P, P, P, P, P, P, P, kda, None) == ERR_SHAPE
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 2, 1, P, P, P, P, P, P, P, P, P, kda, None) == ERR_UNSUP
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 2, P, P, P, P, P, P, P, P, P, kda, None) == ERR_UNSUP
+    g8 = ctypes.c_void_p(264)  # 8-byte aligned: fine for GDA gates, not for KDA's 16-byte pieces
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, P, P, P, P, g8, P, P, P, P, kda, None) == ERR_UNSUP
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, P, P, P, P, P, P, P, P, P, kda - 1, None) == ERR_WS
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 0, 0, P, P, P, P, P, P, P, P, P, f32 - 1, None) == ERR_WS
+    assert pv(0, 300, 4, 2, 0, 128, 128, 64, 1, 1, N, P, P, P, P, P, P, P, N, 0, None) == OK
+
+
 def test_prefill_snapshots_validation(lib):
     need = lib.gdn_prefill_workspace_size(2, 100, 4, 128, 128, 64)
     ps = lib.gdn_prefill_chunked_snapshots

@@ -102,3 +102,62 @@ def test_prefill_varlen_clamps_malformed_offsets():
     # the emptied sequences 1 and 3 kept their initial states
     assert np.array_equal(bits(outs[0][1][1]), bits(state[1]))
     assert np.array_equal(bits(outs[0][1][3]), bits(state[3]))
+
+
+# the general entry point: KDA gates and float32 inputs on packed sequences
+EX_CASES = [
+    # lengths, H, H_qk, d, head map, gate, q/k/v type
+    ([0, 1, 63, 64, 65, 200, 7, 0], 4, 2, 128, "grouped", "kda", "bf16"),
+    ([130, 0, 64, 97], 6, 3, 64, "tiled", "kda", "f32"),
+    ([150, 33, 0, 64], 4, 4, 128, "grouped", "gda", "f32"),
+]
+
+
+def _upload_ex(vc: gi.VarlenCase):
+    t = torch.bfloat16 if vc.qkv_dtype == "bf16" else torch.float32
+    return dict(q=dev(vc.q, t), k=dev(vc.k, t), v=dev(vc.v, t), g=dev(vc.g), beta=dev(vc.beta),
+                state=dev(vc.state), cu=dev(vc.cu_seqlens))
+
+
+@pytest.mark.parametrize("lengths,H,Hq,d,head_map,gate,dt", EX_CASES)
+def test_prefill_varlen_ex(lengths, H, Hq, d, head_map, gate, dt):
+    vc = gi.make_varlen_case(lengths, H, d, H_qk=Hq, seed=800 + sum(lengths), gate=gate, qkv_dtype=dt)
+    u = _upload_ex(vc)
+    st = u["state"].clone()
+    o = torch.full((vc.total, vc.H, vc.d), float("nan"), device="cuda")
+    gdn = _gdn()
+    gdn.gdn_prefill_chunked_varlen_ex(u["cu"], u["q"], u["k"], u["v"], u["g"], u["beta"], st,
+                                      head_map=head_map, o=o)
+    torch.cuda.synchronize()
+    for i, n in enumerate(lengths):
+        a, b = int(vc.cu_seqlens[i]), int(vc.cu_seqlens[i + 1])
+        if n == 0:
+            assert np.array_equal(bits(st[i]), vc.state[i].view(np.int32))
+            continue
+        c = vc.sequence(i)
+        ro, rst, _ = oracle.forward(*[c.f64(x) for x in ("q", "k", "v", "g", "beta")], c.f64("state"),
+                                    head_map=head_map, kda=gate == "kda")
+        eo = rel_err(o[a:b], ro[0], f"seq{i} o")
+        es = rel_err(st[i], rst[0, :, 0], f"seq{i} state")
+        print(f"{gate} {dt} seq {i} len {n}: o {eo:.2e} state {es:.2e}", flush=True)
+        assert eo <= 1e-2 and es <= 1e-2
+        # bit for bit with the general entry point on the sequence alone
+        s1 = dev(vc.state[i][None])
+        o1 = gdn.gdn_prefill_chunked_ex(u["q"][a:b][None].contiguous(), u["k"][a:b][None].contiguous(),
+                                        u["v"][a:b][None].contiguous(), u["g"][a:b][None].contiguous(),
+                                        u["beta"][a:b][None].contiguous(), s1, head_map=head_map)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o[a:b]), bits(o1[0]))
+        assert np.array_equal(bits(st[i]), bits(s1[0]))
+
+
+def test_prefill_varlen_ex_equals_varlen_for_bf16_gda():
+    vc = gi.make_varlen_case([0, 1, 63, 64, 65, 200, 7, 0], 4, 128, H_qk=2, seed=901)
+    u = _upload(vc)
+    o0, s0 = _run(vc, u, "grouped")
+    st = u["state"].clone()
+    o = torch.full((vc.total, vc.H, vc.d), float("nan"), device="cuda")
+    _gdn().gdn_prefill_chunked_varlen_ex(u["cu"], u["q"], u["k"], u["v"], u["g"], u["beta"], st, o=o)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o), bits(o0))
+    assert np.array_equal(bits(st), bits(s0))
