@@ -161,3 +161,28 @@ def test_prefill_varlen_ex_equals_varlen_for_bf16_gda():
     torch.cuda.synchronize()
     assert np.array_equal(bits(o), bits(o0))
     assert np.array_equal(bits(st), bits(s0))
+
+
+def test_prefill_varlen_many_sequences():
+    # 40 sequences of a seeded log-uniform length mix (some below one chunk,
+    # some several chunks) plus two empty ones, through the general entry point
+    lengths = gi.varlen_lengths(2600, 40, seed=31)
+    lengths = lengths[:7] + [0] + lengths[7:29] + [0] + lengths[29:]
+    vc = gi.make_varlen_case(lengths, 4, 64, H_qk=2, seed=33)
+    u = _upload(vc)
+    st = u["state"].clone()
+    o = torch.full((vc.total, vc.H, vc.d), float("nan"), device="cuda")
+    _gdn().gdn_prefill_chunked_varlen_ex(u["cu"], u["q"], u["k"], u["v"], u["g"], u["beta"], st, o=o)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, n in enumerate(lengths):
+        a, b = int(vc.cu_seqlens[i]), int(vc.cu_seqlens[i + 1])
+        if n == 0:
+            assert np.array_equal(bits(st[i]), vc.state[i].view(np.int32))
+            continue
+        c = vc.sequence(i)
+        ro, rst, _ = oracle.forward(*[c.f64(x) for x in ("q", "k", "v", "g", "beta")], c.f64("state"))
+        e = max(rel_err(o[a:b], ro[0], f"seq{i} o"), rel_err(st[i], rst[0, :, 0], f"seq{i} state"))
+        worst = max(worst, e)
+        assert e <= 1e-2, (i, n, e)
+    print(f"{len(lengths)} sequences ({min(lengths)}..{max(lengths)} tokens): worst {worst:.2e}", flush=True)
