@@ -1538,19 +1538,26 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     {
         // ======================= storer wavefront ==========================
+        constexpr int kNonTemporal = 2;  // buffer store cache policy: nt
         // chunk n's output block from sO to o: lane -> row lane / 4 + 16 i,
-        // columns 4 (lane % 4) + 0..3 of the block, read as two 8-byte halves
-        float* const obase = o + (static_cast<size_t>(start) * H + h) * DV + cb * 16 + 4 * (lane & 3);
+        // columns 4 (lane % 4) + 0..3 of the block, read as two 8-byte halves.
+        // The stores go through a buffer view of the chunk's rows with the
+        // non-temporal bit: nothing reads o again here, and the prefill ran
+        // 3.5 us faster than with plain stores, which keep the lines in L2.
         auto store_o = [&](int n, int i0) {  // rows 16 i + lane / 4, i = i0, i0 + 1
+            const int rows = min(kC, len - n * kC);
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(o + ((static_cast<size_t>(start) + n * kC) * H + h) * DV + cb * 16,
+                          ((rows - 1) * H * DV + 16) * 4);
 #pragma unroll
             for (int i = i0; i < i0 + 2; ++i) {
                 const int rr = 16 * i + (lane >> 2);
                 const float* src = &sO[rr][4 * (lane & 3)];
                 const f32x2 a = *reinterpret_cast<const f32x2*>(src);
                 const f32x2 c = *reinterpret_cast<const f32x2*>(src + 2);
-                const int tok = n * kC + rr;  // token of the sequence
-                if (tok < len)
-                    *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(tok) * H * DV) = f32x4{a[0], a[1], c[0], c[1]};
+                if (rr < rows)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{a[0], a[1], c[0], c[1]}),
+                                                           ro, (rr * H * DV + 4 * (lane & 3)) * 4, 0, kNonTemporal);
             }
         };
         // half of the block after B1, half after B2: sO is rewritten after B3
