@@ -186,3 +186,30 @@ def test_prefill_varlen_many_sequences():
         worst = max(worst, e)
         assert e <= 1e-2, (i, n, e)
     print(f"{len(lengths)} sequences ({min(lengths)}..{max(lengths)} tokens): worst {worst:.2e}", flush=True)
+
+
+def test_prefill_varlen_beyond_one_table_block():
+    # 300 sequences: the device table of sanitised starts and chunk offsets is
+    # built 64 offsets at a time, carrying the running maximum and the chunk
+    # count from block to block; many sequences are shorter than a chunk and
+    # some are empty, at positions on both sides of the block edges
+    lengths = gi.varlen_lengths(9000, 290, seed=51)
+    for pos in (0, 63, 64, 65, 127, 128, 200, 250, 280, 299):
+        lengths.insert(pos, 0)
+    assert len(lengths) == 300
+    vc = gi.make_varlen_case(lengths, 2, 64, seed=53)
+    u = _upload(vc)
+    o, st = _run(vc, u, "grouped")
+    worst = 0.0
+    for i, n in enumerate(lengths):
+        a, b = int(vc.cu_seqlens[i]), int(vc.cu_seqlens[i + 1])
+        if n == 0:
+            assert np.array_equal(bits(st[i]), vc.state[i].view(np.int32)), i
+            continue
+        c = vc.sequence(i)
+        ro, rst, _ = oracle.forward(*[c.f64(x) for x in ("q", "k", "v", "g", "beta")], c.f64("state"))
+        e = max(rel_err(o[a:b], ro[0], f"seq{i} o"), rel_err(st[i], rst[0, :, 0], f"seq{i} state"))
+        worst = max(worst, e)
+        assert e <= 1e-2, (i, n, e)
+    assert not torch.isnan(o).any()  # every row belongs to a sequence and is written
+    print(f"{len(lengths)} sequences ({min(lengths)}..{max(lengths)} tokens): worst {worst:.2e}", flush=True)
