@@ -151,3 +151,25 @@ def test_prefill_in_place_graph_replays(entry, gate):
     else:
         call = lambda: gdn.gdn_prefill_chunked_ex_noalloc(u["q"], u["k"], u["v"], u["g"], u["beta"], state, o)
     _in_place_replays(call, state, o, s0)
+
+
+@pytest.mark.parametrize("gate", ["gda", "kda"])
+def test_prefill_varlen_graph_replays(gate):
+    # packed sequences: the device table of sequence starts is built inside the
+    # captured work, from offsets that stay on the device
+    lengths = [0, 70, 1, 130, 64, 0, 9]
+    vc = gi.make_varlen_case(lengths, 4, 64, seed=75, gate=gate)
+    bf = torch.bfloat16
+    q, k, v = (torch.from_numpy(x).to(bf).cuda() for x in (vc.q, vc.k, vc.v))
+    g, beta = torch.from_numpy(vc.g).cuda(), torch.from_numpy(vc.beta).cuda()
+    cu = torch.from_numpy(vc.cu_seqlens).cuda()
+    state = torch.from_numpy(vc.state).cuda()
+    s0 = state.clone()
+    o = torch.zeros((vc.total, vc.H, vc.d), device="cuda")
+    gdn = _gdn()
+    code = gdn.GDN_GATE_KEY if gate == "kda" else gdn.GDN_GATE_HEAD
+    ws = torch.empty(gdn.gdn_prefill_varlen_workspace_size_ex(len(lengths), vc.total, vc.H, vc.d, vc.d, 64,
+                                                               gdn.GDN_BF16, code),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: gdn.gdn_prefill_chunked_varlen_ex(cu, q, k, v, g, beta, state, o=o, workspace=ws)
+    _in_place_replays(call, state, o, s0)
