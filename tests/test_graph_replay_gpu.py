@@ -173,3 +173,35 @@ def test_prefill_varlen_graph_replays(gate):
                      dtype=torch.uint8, device="cuda")
     call = lambda: gdn.gdn_prefill_chunked_varlen_ex(cu, q, k, v, g, beta, state, o=o, workspace=ws)
     _in_place_replays(call, state, o, s0)
+
+
+@pytest.mark.parametrize("gate", ["gda", "kda"])
+def test_prefill_snapshots_graph_replays(gate):
+    # the chunked path with K = 5 slots and a final state (slots 1..4 after
+    # tokens 1..4, the final state after all 90)
+    c = gi.make_case(2, 90, 2, 128, K=5, gate=gate, qkv_dtype="bf16", seed=76)
+    u = upload(c)
+    state = u["state"]
+    s0 = state.clone()
+    fin = torch.zeros((c.B, c.H, c.d_k, c.d_v), device="cuda")
+    o = torch.empty((c.B, c.T, c.H, c.d_v), device="cuda")
+    gdn = _gdn()
+    code = gdn.GDN_GATE_KEY if gate == "kda" else gdn.GDN_GATE_HEAD
+    ws = torch.empty(gdn.gdn_prefill_workspace_size_ex(c.B, c.T, c.H, 128, 128, 64, gdn.GDN_BF16, code),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: gdn.gdn_prefill_chunked_ex(u["q"], u["k"], u["v"], u["g"], u["beta"], state, final_state=fin,
+                                              o=o, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = (bits(state), bits(o), bits(fin))
+    g = _capture(call)
+    for i in range(REPLAYS):
+        state.copy_(s0)
+        fin.fill_(float("nan"))
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(state), ref[0]), f"snapshots after replay {i}"
+        assert np.array_equal(bits(o), ref[1]), f"o after replay {i}"
+        assert np.array_equal(bits(fin), ref[2]), f"final state after replay {i}"
