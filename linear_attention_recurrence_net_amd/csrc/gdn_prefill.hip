@@ -112,7 +112,7 @@ struct WsL : std::conditional_t<KDA, WsKda<DK>, Ws<DK>> {
     static constexpr int kImgV = kC * DV * 2;  // the V image
     static constexpr int kKI = KDA ? WsKda<DK>::kKG : Base::kBlock;        // K image the chain reads
     static constexpr int kQI = KDA ? WsKda<DK>::kQG : Base::kBlock + kImg; // Q image the chain reads
-    static constexpr int kVI = Base::kBlock + (KDA ? 0 : 2 * kImg);         // V image (F32)
+    static constexpr int kVI = Base::kBlock + (KDA ? 0 : 2 * kImg);         // V image (F32), by column block
     static constexpr int kBlock = F32 ? kVI + kImgV : Base::kBlock;
     static_assert(kBlock % 256 == 0, "workspace blocks stay 256-byte aligned");
 };
@@ -454,7 +454,11 @@ __device__ __forceinline__ bf16x8 ld8_in(const void* base, size_t elem) {
 }
 
 // Float32 inputs: the chunk's V rows of head h as a bf16 image (zero past
-// the sequence end), lane -> rows 16 t + l%16, columns 8 (l/16) + 32 c ...
+// the sequence end), lane -> rows 16 t + l%16, columns 8 (l/16) + 32 c ....
+// The image is stored by column block, [DV/16][64 rows][16 columns], so
+// that each chain workgroup reads its block as one contiguous 2 KiB piece
+// (row-major, its 32 bytes of every row shared their cache lines with the
+// other column blocks, and the float32-input prefill took 4 us longer).
 template <class L, int DV>
 __device__ __forceinline__ void store_v_image(const void* v, char* wsb, size_t t0, int nvalid, int H,
                                               int h, int lane) {
@@ -466,7 +470,7 @@ __device__ __forceinline__ void store_v_image(const void* v, char* wsb, size_t t
         for (int c = 0; c < DV / 32; ++c) {
             const int d0 = 32 * c + 8 * grp;
             const bf16x8 x = r < nvalid ? ld8_in<true>(v, ((t0 + r) * H + h) * DV + d0) : zero_bf16x8();
-            *reinterpret_cast<bf16x8*>(wsb + L::kVI + (static_cast<size_t>(r) * DV + d0) * 2) = x;
+            *reinterpret_cast<bf16x8*>(wsb + L::kVI + ((d0 / 16) * kC + r) * 32 + (d0 % 16) * 2) = x;
         }
     }
 }
@@ -1150,10 +1154,10 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const int r0 = n * kC;
             __amdgpu_buffer_rsrc_t rv;
             int rowb, off0;
-            if constexpr (F32) {  // the workspace's bf16 V image
+            if constexpr (F32) {  // the workspace's bf16 V image, this column block's piece
                 rv = ws_rsrc(n);
-                rowb = DV * 2;
-                off0 = L::kVI + cb * 32;
+                rowb = 32;
+                off0 = L::kVI + cb * kC * 32;
             } else {
                 const int row_b16 = H * DV * 2;
                 rv = make_rsrc(v + (static_cast<size_t>(start + r0) * H + h) * DV,
