@@ -101,10 +101,10 @@ struct WsKda : Ws<DK> {
 };
 // Workspace block of one (sequence, head, chunk) for each gate kind and input
 // type.  With float32 q/k/v the prep also rounds the chunk's K, Q and V rows
-// to bf16 images, row-major [64][DK] for K and Q and [64][DV] for V (zero
-// past the sequence end), which the
-// chain reads in place of the inputs; KDA's decayed KG and QG already are
-// such images, so KDA adds only V.
+// to bf16 images (zero past the sequence end), row-major [64][DK] for K and Q
+// and by column block [DV/16][64][16] for V, which the chain reads in place
+// of the inputs; KDA's decayed KG and QG already are such images, so KDA adds
+// only V.
 template <int DK, int DV, bool KDA, bool F32>
 struct WsL : std::conditional_t<KDA, WsKda<DK>, Ws<DK>> {
     using Base = std::conditional_t<KDA, WsKda<DK>, Ws<DK>>;
