@@ -240,6 +240,24 @@ def _timing(region_ms, eager_ms, steps):
     return dict(ms_per_step=per, us_per_launch=per * 1e3, eager_us_per_launch=eager_ms * 1e3)
 
 
+def bench_copy_context(torch, steps, warmup):
+    """A plain device-to-device copy of 64 MiB (torch's copy_), timed like the
+    decode: graph-replayed launches over 8 rotating source/destination pairs
+    (1 GiB), so each copy reads and writes HBM.  Context for the decode's
+    fraction of peak: what a copy of the decode's state size reaches here."""
+    n = 16 * 1024 * 1024
+    pairs = [(torch.randn(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(8)]
+    calls = [lambda sp, s=s, d=d: d.copy_(s) for s, d in pairs]
+    t = _timing(*run_timed(torch, calls, steps, warmup), steps)
+    nbytes = 2 * n * 4
+    gbs = nbytes / (t["us_per_launch"] * 1e-6) / 1e9
+    del pairs, calls
+    torch.cuda.empty_cache()
+    return {"what": "device-to-device copy of 64 MiB (torch copy_), 8 rotating pairs, graph-replayed",
+            "bytes_per_copy": nbytes, "us_per_copy": t["us_per_launch"], "achieved_gbs": gbs,
+            "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
 def bench_decode(torch, lib, steps, warmup):
     import gdn_inputs as gi
     case = gi.workload_case(1)
@@ -648,6 +666,8 @@ def main():
         dec = bench_decode(torch, lib, args.steps, args.warmup)
         log(f"decode: {dec['us_per_launch']:.2f} us/launch, {dec['achieved_gbs']:.0f} GB/s "
             f"(eager {dec['eager_us_per_launch']:.2f} us)")
+        copy_ctx = bench_copy_context(torch, min(args.steps, 100), min(args.warmup, 10))
+        log(f"copy context: {copy_ctx['us_per_copy']:.2f} us per 64 MiB copy, {copy_ctx['achieved_gbs']:.0f} GB/s")
     if args.copy_calibration:
         log("copy calibration: 20 x 64 MiB device copies ...")
         src = torch.randn(16 * 1024 * 1024, device="cuda")
@@ -747,6 +767,7 @@ def main():
             "launch_us_p10_p50_p90": [round(x, 3) for x in dec["spread_us"]],
         },
         "cpu_baseline": cpu,
+        "copy_context": copy_ctx,
         "paths": paths,
     }
     print(json.dumps(line), flush=True)
