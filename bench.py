@@ -337,6 +337,9 @@ def bench_verify(torch, lib, cfg, steps, warmup):
     kda = case.gate == "kda"
     vt = _timing(*run_timed(torch, fwd, steps, warmup), steps)
     rt = _timing(*run_timed(torch, rbs, steps, warmup), steps)
+    # one event pair per eager launch, 100 launches (the graph mean is the figure)
+    vt["launch_us_p10_p50_p90"] = [round(x, 3) for x in launch_spread(torch, fwd)]
+    rt["launch_us_p10_p50_p90"] = [round(x, 3) for x in launch_spread(torch, rbs)]
     bt = _timing(*run_timed(torch, pair, steps, warmup), steps)
     vbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, case.K, kda, True)
     moved = int(np.count_nonzero(case.accepted > 0))
@@ -414,6 +417,8 @@ def _bench_prefill_leg(torch, lib, case, entry, ws_bytes, steps, warmup):
     # Cache then holds: for comparison with single-set timings, never `value`
     warm = _timing(*run_timed(torch, calls[:1], steps, warmup), steps)
     t["single_set_us_per_launch"] = warm["us_per_launch"]
+    # one event pair per eager launch, 100 launches (the graph mean is the figure)
+    t["launch_us_p10_p50_p90"] = [round(x, 3) for x in launch_spread(torch, calls)]
     n_sets = len(sets)
     del sets, calls
     torch.cuda.empty_cache()
@@ -469,9 +474,11 @@ def bench_prefill_varlen(torch, lib, steps, warmup):
             if st_ != 0:
                 raise RuntimeError(f"libgdn status {st_}")
         return call
-    tm = _timing(*run_timed(torch, [mk(s) for s in sets], steps, warmup), steps)
+    vcalls = [mk(s) for s in sets]
+    tm = _timing(*run_timed(torch, vcalls, steps, warmup), steps)
+    tm["launch_us_p10_p50_p90"] = [round(x, 3) for x in launch_spread(torch, vcalls)]
     n_sets = len(sets)
-    del sets
+    del sets, vcalls
     torch.cuda.empty_cache()
     sec = tm["us_per_launch"] * 1e-6
     # per sequence: tokens as in the single-sequence prefill, plus its own state in and out
