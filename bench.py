@@ -334,6 +334,20 @@ def bench_verify(torch, lib, cfg, steps, warmup):
             r(stream)
         return call
     pair = [both(f, r) for f, r in zip(fwd, rbs)]
+
+    def fused_call(s):
+        # the rollback of the previous draft fused into the next verification
+        dt = 1 if case.qkv_dtype == "bf16" else 0
+        args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, dt, 1 if case.gate == "kda" else 0, case.K,
+                vp(acc), vp(s["q"]), vp(s["k"]), vp(s["v"]), vp(s["g"]), vp(s["beta"]), vp(s["state"]), None,
+                vp(s["o"]), None)
+
+        def call(stream):
+            st = lib.gdn_forward_snapshots_after_rollback(*args, stream)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+        return call
+    fused = [fused_call(s) for s in sets]
     kda = case.gate == "kda"
     vt = _timing(*run_timed(torch, fwd, steps, warmup), steps)
     rt = _timing(*run_timed(torch, rbs, steps, warmup), steps)
@@ -341,6 +355,7 @@ def bench_verify(torch, lib, cfg, steps, warmup):
     vt["launch_us_p10_p50_p90"] = [round(x, 3) for x in launch_spread(torch, fwd)]
     rt["launch_us_p10_p50_p90"] = [round(x, 3) for x in launch_spread(torch, rbs)]
     bt = _timing(*run_timed(torch, pair, steps, warmup), steps)
+    ft = _timing(*run_timed(torch, fused, steps, warmup), steps)
     vbytes = recurrent_bytes(case.B, case.T, case.H, case.d_k, case.K, kda, True)
     moved = int(np.count_nonzero(case.accepted > 0))
     rbytes = 2 * moved * case.H * 4 * case.d_k * case.d_v
@@ -354,9 +369,12 @@ def bench_verify(torch, lib, cfg, steps, warmup):
         rollback=dict(bytes=rbytes, sequences_rolled=moved, achieved_gbs=rg,
                       frac_of_hbm_peak=rg / HBM_PEAK_GBS, **rt),
         verify_plus_rollback=dict(tokens_per_s=tokens / (bt["us_per_launch"] * 1e-6), **bt),
+        # gdn_forward_snapshots_after_rollback: the same two steps in one launch
+        rollback_fused_into_verify=dict(tokens_per_s=tokens / (ft["us_per_launch"] * 1e-6),
+                                        bytes=vbytes + rbytes // 2, **ft),
         rotating_sets=len(sets),
     )
-    del sets, fwd, rbs, pair
+    del sets, fwd, rbs, pair, fused
     torch.cuda.empty_cache()
     return out
 
@@ -690,7 +708,9 @@ def main():
             r = bench_verify(torch, lib, cfg, args.steps, args.warmup)
             paths[f"verify_rollback_{'gda' if cfg == 2 else 'kda'}"] = r
             log(f"  verify {r['verify']['us_per_launch']:.2f} us {r['verify']['achieved_gbs']:.0f} GB/s; "
-                f"rollback {r['rollback']['us_per_launch']:.2f} us {r['rollback']['achieved_gbs']:.0f} GB/s")
+                f"rollback {r['rollback']['us_per_launch']:.2f} us {r['rollback']['achieved_gbs']:.0f} GB/s; "
+                f"both {r['verify_plus_rollback']['us_per_launch']:.2f} us, "
+                f"fused {r['rollback_fused_into_verify']['us_per_launch']:.2f} us")
     if args.only in ("broadcast", "all"):
         log("decode with shared q/k heads ...")
         paths["decode_qk_broadcast_gda"] = r = bench_decode_broadcast(torch, lib, args.steps, args.warmup)

@@ -112,6 +112,33 @@ int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_
                         const int32_t* accepted, float* state, int32_t* err_flag, void* stream);
 
 /*
+ * The rollback of the previous draft fused into the next verification: the
+ * results of gdn_rollback_select(accepted) followed by
+ * gdn_forward_qk_broadcast on the same state, in one launch (koboldcpp
+ * commit log, tag v1.113.1, bullets "llama: allow partial seq_rm for GDN
+ * models for speculative decoding" and "metal: add GDN partial rollback":
+ * the accepted intermediate state becomes the input of the next step).
+ * For each sequence b with a = accepted[b] in 1..K-1, every head reads its
+ * input state from slot a and also copies it to slot 0, bit for bit; a == 0
+ * reads slot 0; an index outside 0..K-1 sets *err_flag (a device int32 the
+ * caller zeroes; may be NULL) and the sequence starts from slot 0, as after
+ * a rollback that left it untouched.  Then slots 1..min(T, K-1), o and
+ * final_state are written as by gdn_forward_qk_broadcast (K = 1: the final
+ * state goes to slot 0).  Every argument, layout and error as there, plus
+ * accepted (device int32 [B]; NULL with B > 0 -> GDN_ERR_NULL).  The
+ * results are bit-identical to the two calls.  With T = 0 or K = 1 (one
+ * slot: nothing to roll back, an index other than 0 is only flagged) the
+ * entry point makes the two calls itself.
+ */
+int gdn_forward_snapshots_after_rollback(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                         int32_t head_map, int32_t d_k, int32_t d_v,
+                                         int32_t qkv_dtype, int32_t gate, int32_t K,
+                                         const int32_t* accepted, const void* q, const void* k,
+                                         const void* v, const float* g, const float* beta,
+                                         float* state, float* final_state, float* o,
+                                         int32_t* err_flag, void* stream);
+
+/*
  * Chunked prefill (llama.cpp commit log, tag b9752, bullet "llama : enable
  * chunked fused GDN path"; the chunk algebra is the WY/UT form of the same
  * recurrence and gives the same result up to rounding).

@@ -8,6 +8,7 @@ library is missing or a tensor is not on the GPU, the call raises.
 
 Entry points (same names as the C ABI):
   gdn_forward, gdn_forward_snapshots, gdn_rollback_select,
+  gdn_forward_snapshots_after_rollback,
   gdn_prefill_workspace_size, gdn_prefill_chunked,
   gdn_forward_qk_broadcast, gdn_prefill_chunked_qk_broadcast,
   gdn_prefill_varlen_workspace_size, gdn_prefill_chunked_varlen,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     gdn_forward,
     gdn_forward_qk_broadcast,
     gdn_forward_snapshots,
+    gdn_forward_snapshots_after_rollback,
     gdn_prefill_chunked,
     gdn_prefill_chunked_qk_broadcast,
     gdn_prefill_chunked_ex,

@@ -20,6 +20,7 @@ EXPORTED = (
     "gdn_forward",
     "gdn_forward_snapshots",
     "gdn_rollback_select",
+    "gdn_forward_snapshots_after_rollback",
     "gdn_prefill_workspace_size",
     "gdn_prefill_chunked",
     "gdn_forward_qk_broadcast",
@@ -74,6 +75,8 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_chunked.argtypes = [i32] * 6 + [vp] * 8 + [sz, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
     lib.gdn_forward_qk_broadcast.argtypes = [i32] * 10 + [vp] * 9
+    lib.gdn_forward_snapshots_after_rollback.argtypes = [i32] * 10 + [vp] * 11
+    lib.gdn_forward_snapshots_after_rollback.restype = ctypes.c_int
     lib.gdn_forward_qk_broadcast.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.argtypes = [i32] * 8 + [vp] * 8 + [sz, vp]
     lib.gdn_prefill_chunked_snapshots.argtypes = [i32] * 9 + [vp] * 9 + [sz, vp]
@@ -296,6 +299,37 @@ def gdn_forward_qk_broadcast(q, k, v, g, beta, state, head_map="grouped", final_
                                             _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                             _ptr(final_state), _ptr(o), _stream_ptr(dev))
     _check("gdn_forward_qk_broadcast", st)
+    return o
+
+
+def gdn_forward_snapshots_after_rollback(accepted, q, k, v, g, beta, state, head_map="grouped",
+                                         final_state=None, o=None, err_flag=None):
+    """gdn_rollback_select(accepted, state, err_flag) followed by
+    gdn_forward_qk_broadcast on state [B,H,K,d_k,d_v], in one launch; returns o."""
+    B, T, H, dk, dv, dt, gate, dev, Hq = _qkv_gate(q, k, v, g, beta, shared_qk=True)
+    hm = _head_map(head_map)
+    _dev_tensor("state", state, (torch.float32,), dev)
+    if state.dim() != 5:
+        raise ValueError("state must be [B,H,K,d_k,d_v]")
+    K = state.shape[2]
+    _shape("state", state, (B, H, K, dk, dv))
+    _dev_tensor("accepted", accepted, (torch.int32,), dev)
+    _shape("accepted", accepted, (B,))
+    if err_flag is not None:
+        _dev_tensor("err_flag", err_flag, (torch.int32,), dev)
+        if err_flag.numel() < 1:
+            raise ValueError("err_flag must hold one int32")
+    if final_state is not None:
+        _dev_tensor("final_state", final_state, (torch.float32,), dev)
+        _shape("final_state", final_state, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _dev_tensor("o", o, (torch.float32,), dev)
+    _shape("o", o, (B, T, H, dv))
+    st = library().gdn_forward_snapshots_after_rollback(
+        B, T, H, Hq, hm, dk, dv, dt, gate, K, _ptr(accepted), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(final_state), _ptr(o), _ptr(err_flag), _stream_ptr(dev))
+    _check("gdn_forward_snapshots_after_rollback", st)
     return o
 
 

@@ -42,6 +42,11 @@ int validate_recurrent(int B, int T, int H, int d_k, int d_v, int qkv_dtype, int
     return GDN_OK;
 }
 
+int launch_forward(int B, int T, int H, int H_qk, int head_map, int d_k, int d_v, int qkv_dtype,
+                   int gate, int K, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float* state, float* final_state, float* o,
+                   const int32_t* accepted, int32_t* err_flag, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +64,44 @@ int gdn_forward_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk, int3
     if (B == 0 || H == 0) return GDN_OK;
     // With no token, nothing changes unless a final_state copy is requested.
     if (T == 0 && final_state == nullptr) return GDN_OK;
+    return launch_forward(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                          final_state, o, nullptr, nullptr, stream);
+}
+
+int gdn_forward_snapshots_after_rollback(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                         int32_t head_map, int32_t d_k, int32_t d_v,
+                                         int32_t qkv_dtype, int32_t gate, int32_t K,
+                                         const int32_t* accepted, const void* q, const void* k,
+                                         const void* v, const float* g, const float* beta,
+                                         float* state, float* final_state, float* o,
+                                         int32_t* err_flag, void* stream) {
+    int st = validate_recurrent(B, T, H, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                final_state, o);
+    if (st != GDN_OK) return st;
+    st = validate_heads(H, H_qk, head_map);
+    if (st != GDN_OK) return st;
+    if (B > 0 && !accepted) return GDN_ERR_NULL;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (T == 0 || K == 1) {
+        // no token, or a single slot (nothing to roll back; an index other
+        // than 0 is only flagged): the two calls themselves
+        st = gdn_rollback_select(B, H, K, d_k, d_v, accepted, state, err_flag, stream);
+        if (st != GDN_OK) return st;
+        return gdn_forward_qk_broadcast(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g,
+                                        beta, state, final_state, o, stream);
+    }
+    return launch_forward(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                          final_state, o, accepted, err_flag, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int launch_forward(int B, int T, int H, int H_qk, int head_map, int d_k, int d_v, int qkv_dtype,
+                   int gate, int K, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float* state, float* final_state, float* o,
+                   const int32_t* accepted, int32_t* err_flag, void* stream) {
     gdn::RecurrentArgs a;
     a.q = q;
     a.k = k;
@@ -80,8 +123,14 @@ int gdn_forward_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk, int3
     a.n_snap = K > 1 ? (T < K - 1 ? T : K - 1) : 0;
     a.bf16 = qkv_dtype == GDN_BF16;
     a.kda = gate == GDN_GATE_KEY;
+    a.accepted = accepted;
+    a.err_flag = err_flag;
     return check_launch(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+extern "C" {
 
 int gdn_forward_snapshots(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                           int32_t qkv_dtype, int32_t gate, int32_t K, const void* q,

@@ -30,6 +30,12 @@ struct RecurrentArgs {
     bool tiled;          // qk_head(h) = tiled ? h % Hqk : h / group
     int n_snap;          // snapshot slots written: K > 1 ? min(T, K-1) : 0
     bool bf16, kda;
+    // Rollback of the previous draft before this call (nullptr: none): the
+    // input state of sequence b is slot accepted[b], which is also copied to
+    // slot 0; an index outside 0..K-1 sets *err_flag (if given) and the
+    // sequence starts from slot 0.
+    const int32_t* accepted = nullptr;
+    int32_t* err_flag = nullptr;
 };
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);

@@ -183,18 +183,22 @@ __device__ __forceinline__ float sum_subgroups(float x) {
 }
 
 // ONE: the launch has exactly one token and no snapshot (plain decode).
+// ROLL: the input state of sequence b is slot accepted[b] (the rollback of
+// the previous draft, fused into this launch), copied to slot 0 as well.
 // DK and DV: key and value head sizes (state rows and columns).  WPH:
 // wavefronts per head, one workgroup per head.  TB > 0: the launch has 1..TB
 // tokens, whose inputs are all loaded before the first token is computed.  Two wavefronts per SIMD are
 // requested (at most 256 registers), so a 1024-head decode grid of 2048
 // wavefronts is resident at once.
-template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB, bool ROLL>
 __global__ void __launch_bounds__((WPH * kWave)) __attribute__((amdgpu_waves_per_eu(2)))
 recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const float* __restrict__ g,
                  const float* __restrict__ beta, float* __restrict__ state,
                  float* __restrict__ final_state, float* __restrict__ o, int T, int H, int K,
-                 int n_snap, int Hqk, int group, bool tiled) {
+                 int n_snap, int Hqk, int group, bool tiled, const int32_t* __restrict__ accepted,
+                 int32_t* __restrict__ err_flag) {
+    static_assert(!(ROLL && ONE), "a fused rollback runs on the multi-token path");
     constexpr int CG = DV / 4;        // lanes across one state row
     constexpr int RS = kWave / CG;    // row sub-groups (rows per load instruction)
     constexpr int RW = DK / WPH;      // rows per wavefront
@@ -243,9 +247,20 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
         load_token(cur, 0);
     }
 
+    // the slot the input state is read from: 0, or with ROLL the accepted
+    // draft length of the sequence (an invalid one is flagged, as by the
+    // rollback, and the sequence starts from slot 0)
+    int src = 0;
+    if constexpr (ROLL) {
+        const int a = accepted[b];
+        if (a >= 0 && a < K)
+            src = a;
+        else if (h == 0 && threadIdx.x == 0 && err_flag != nullptr)
+            atomicOr(err_flag, 1);
+    }
     f32x4 s[L];
     {
-        const TileIO<DK, DV, ONE> in(slots);
+        const TileIO<DK, DV, ONE> in(slots + static_cast<size_t>(src) * TILE);
 #pragma unroll
         for (int i = 0; i < L; ++i) s[i] = in.load(off0, i);
     }
@@ -256,6 +271,17 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     // drain the previous token's snapshot stores.  After it, the in-loop
     // waits cover only the prefetched inputs and the stores stay in flight.
     if (!ONE) __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (ROLL) {
+        // the rollback itself: slot 0 <- slot src, bit for bit.  No wavefront
+        // of the head reads slot 0 here, and the snapshot slots (src among
+        // them) are written only after the first token's exchange, which
+        // every wavefront of the head reaches with all of its rows loaded.
+        if (src != 0) {
+            const TileIO<DK, DV, ONE> out(slots);
+#pragma unroll
+            for (int i = 0; i < L; ++i) out.store(off0, i, s[i]);
+        }
+    }
     const bool keep_last = K == 1 || final_state != nullptr;
 
     // One token from its inputs `cur`: the folded update of the row block,
@@ -448,12 +474,12 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
 }
 
-template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB = 0>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB = 0, bool ROLL = false>
 static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH, TB>), grid, dim3(WPH * kWave), 0, stream,
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH, TB, ROLL>), grid, dim3(WPH * kWave), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
-                       a.n_snap, a.Hqk, a.group, a.tiled);
+                       a.n_snap, a.Hqk, a.group, a.tiled, a.accepted, a.err_flag);
 }
 
 // Heads that one round of the single-token 128 x 128 kernel holds at two
@@ -482,6 +508,16 @@ constexpr int heads_split(int wph) { return KDA && DK / wph > kWave ? DK / kWave
 
 template <int DK, int DV, bool KDA, bool BF16>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+    if (a.accepted != nullptr) {
+        // rollback fused into the launch: the multi-token shapes, any T >= 1
+        constexpr int WPH = heads_split<DK, KDA>(DK == 128 && DV == 128 ? kWphMulti128 : kWphMulti);
+        constexpr bool DRAFT = DK == 128 && DV == 128;
+        if (DRAFT && a.T >= 1 && a.T <= kDraft)
+            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, DRAFT ? kDraft : 0, true>(a, stream);
+        else
+            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, 0, true>(a, stream);
+        return hipGetLastError();
+    }
     if (a.T == 1 && a.n_snap == 0) {
         // Single token: two wavefronts per head while the grid fits one
         // resident round (64 MiB of 128 x 128 state: 23.7 us against 25.1 us

@@ -22,6 +22,7 @@ def main(path):
         "gdn_forward": ([i32] * 7 + [vp] * 8, ctypes.c_int),
         "gdn_forward_snapshots": ([i32] * 8 + [vp] * 9, ctypes.c_int),
         "gdn_rollback_select": ([i32] * 5 + [vp] * 4, ctypes.c_int),
+        "gdn_forward_snapshots_after_rollback": ([i32] * 10 + [vp] * 11, ctypes.c_int),
         "gdn_prefill_workspace_size": ([i32] * 6, sz),
         "gdn_prefill_chunked": ([i32] * 6 + [vp] * 8 + [sz, vp], ctypes.c_int),
         "gdn_forward_qk_broadcast": ([i32] * 10 + [vp] * 9, ctypes.c_int),
@@ -62,6 +63,10 @@ def main(path):
     expect(rb(1, 1, 4, 64, 64, N, P, N, N), ERR_NULL, "rollback accepted NULL")
     expect(rb(1, 1, 4, 3, 3, P, P, N, N), ERR_UNSUP, "rollback odd tile")
     expect(rb(0, 1, 4, 64, 64, P, P, N, N), OK, "rollback B = 0")
+    far = lib.gdn_forward_snapshots_after_rollback
+    expect(far(1, 1, 1, 1, 0, 64, 64, 1, 0, 4, N, P, P, P, P, P, P, N, P, N, N), ERR_NULL, "fused accepted NULL")
+    expect(far(1, 1, 4, 3, 0, 64, 64, 1, 0, 4, P, P, P, P, P, P, P, N, P, N, N), ERR_SHAPE, "fused H_qk")
+    expect(far(0, 1, 1, 1, 0, 64, 64, 1, 0, 4, N, P, P, P, P, P, P, N, P, N, N), OK, "fused B = 0")
     # prefill entry points
     need = lib.gdn_prefill_workspace_size(1, 100, 2, 128, 128, 64)
     expect(need > 0, True, "workspace size")

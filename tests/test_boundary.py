@@ -94,6 +94,24 @@ def test_snapshot_validation(lib):
     assert snap(lib, K=4, B=0) == OK
 
 
+def test_forward_after_rollback_validation(lib):
+    def far(B=1, T=1, H=1, Hq=1, hm=0, dk=64, dv=64, dt=1, gate=0, K=4, acc=P, q=P, k=P, v=P, g=P, beta=P,
+            st=P, fin=N, o=P, err=N):
+        return lib.gdn_forward_snapshots_after_rollback(B, T, H, Hq, hm, dk, dv, dt, gate, K, acc, q, k, v, g,
+                                                        beta, st, fin, o, err, None)
+    assert far(acc=N) == ERR_NULL
+    assert far(st=N) == ERR_NULL
+    assert far(q=N) == ERR_NULL
+    assert far(K=0) == ERR_SHAPE
+    assert far(H=4, Hq=3) == ERR_SHAPE
+    assert far(hm=2) == ERR_UNSUP
+    assert far(dk=96) == ERR_UNSUP
+    assert far(gate=2) == ERR_UNSUP
+    assert far(o=ctypes.c_void_p(264)) == ERR_UNSUP
+    assert far(B=0, acc=N) == OK
+    assert far(H=0) == OK
+
+
 def test_rollback_validation(lib):
     rb = lib.gdn_rollback_select
     assert rb(1, 1, 4, 64, 64, N, P, N, None) == ERR_NULL

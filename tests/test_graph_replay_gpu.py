@@ -205,3 +205,20 @@ def test_prefill_snapshots_graph_replays(gate):
         assert np.array_equal(bits(state), ref[0]), f"snapshots after replay {i}"
         assert np.array_equal(bits(o), ref[1]), f"o after replay {i}"
         assert np.array_equal(bits(fin), ref[2]), f"final state after replay {i}"
+
+
+@pytest.mark.parametrize("gate,d", [("gda", 128), ("kda", 64)])
+def test_rollback_fused_into_verify_graph_replays(gate, d):
+    c = gi.make_case(6, 4, 4, d, K=4, gate=gate, qkv_dtype="bf16", seed=77)
+    u = upload(c)
+    state = u["state"]
+    state[:, :, 1:] = torch.randn_like(state[:, :, 1:])
+    s0 = state.clone()
+    o = torch.empty((c.B, c.T, c.H, c.d_v), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc = torch.tensor([0, 1, 2, 3, 3, 1], dtype=torch.int32, device="cuda")
+    gdn = _gdn()
+    call = lambda: gdn.gdn_forward_snapshots_after_rollback(acc, u["q"], u["k"], u["v"], u["g"], u["beta"], state,
+                                                            o=o, err_flag=err)
+    _in_place_replays(call, state, o, s0)
+    assert int(err.item()) == 0
