@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "0a6d8b05d61c4b1d824136dda672f35529e9edb6db375f6f2690d1ca83e726e6",
-    "fetch_kib": 33263.5,       # median over 62 decode dispatches
-    "write_kib": 66086.125,
+    "sha256": "4fcc1fb85fb5de6845d6454b42999af9a582b3677dc849ef1981e75e7aacbc55",
+    "fetch_kib": 33266.5,       # median over 62 decode dispatches
+    "write_kib": 66085.6875,
     "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
