@@ -519,9 +519,10 @@ def bench_prefill_snapshots(torch, lib, steps, warmup):
     snapshot kernel timed on the same inputs beside it."""
     import gdn_inputs as gi
     w = SNAP_WORKLOAD
-    case = gi.make_case(w["B"], w["T"], w["H"], w["d"], K=w["K"], qkv_dtype="bf16", seed=13)
+    case = gi.make_case(w["B"], w["T"], w["H"], w["d"], K=w["K"], qkv_dtype="bf16", seed=13, with_accepted=True)
     d = upload_case(torch, case)
     sets = _rotating_sets(torch, d, case)
+    acc = torch.from_numpy(case.accepted).to("cuda")
     ws_bytes = lib.gdn_prefill_workspace_size(case.B, case.T, case.H, case.d_k, case.d_v, 64)
     for s in sets:
         s["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
@@ -537,7 +538,31 @@ def bench_prefill_snapshots(torch, lib, steps, warmup):
             if st != 0:
                 raise RuntimeError(f"libgdn status {st}")
         return call
+    def rolled_then_chunked(s):
+        rb = (case.B, case.H, case.K, case.d_k, case.d_v, vp(acc), vp(s["state"]), None)
+        ch = chunked(s)
+
+        def call(stream):
+            st = lib.gdn_rollback_select(*rb, stream)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+            ch(stream)
+        return call
+
+    def fused(s):
+        # the rollback of the previous draft fused into the chunked verification
+        args = (case.B, case.T, case.H, case.H, 0, case.d_k, case.d_v, 64, 1, 0, case.K, vp(acc), vp(s["q"]),
+                vp(s["k"]), vp(s["v"]), vp(s["g"]), vp(s["beta"]), vp(s["state"]), None, vp(s["o"]),
+                vp(s["ws"]), ws_bytes, None)
+
+        def call(stream):
+            st = lib.gdn_prefill_chunked_ex_after_rollback(*args, stream)
+            if st != 0:
+                raise RuntimeError(f"libgdn status {st}")
+        return call
     ct = _timing(*run_timed(torch, [chunked(s) for s in sets], steps, warmup), steps)
+    bt = _timing(*run_timed(torch, [rolled_then_chunked(s) for s in sets], steps, warmup), steps)
+    ft = _timing(*run_timed(torch, [fused(s) for s in sets], steps, warmup), steps)
     rec = [raw_forward_call(lib, case, s, s["state"], s["o"], K=case.K) for s in sets]
     rt = _timing(*run_timed(torch, rec, steps, warmup), steps)
     nb = recurrent_bytes(case.B, case.T, case.H, case.d_k, case.K, False, True)
@@ -547,6 +572,10 @@ def bench_prefill_snapshots(torch, lib, steps, warmup):
         gbs = nb / (t["us_per_launch"] * 1e-6) / 1e9
         out[key] = dict(tokens_per_s=tokens / (t["us_per_launch"] * 1e-6), achieved_gbs=gbs,
                         frac_of_hbm_peak=gbs / HBM_PEAK_GBS, **t)
+    # rollback (accepted lengths drawn with the inputs) then the chunked call,
+    # as two launches and as gdn_prefill_chunked_ex_after_rollback
+    out["rollback_then_chunked"] = dict(tokens_per_s=tokens / (bt["us_per_launch"] * 1e-6), **bt)
+    out["rollback_fused_into_chunked"] = dict(tokens_per_s=tokens / (ft["us_per_launch"] * 1e-6), **ft)
     del sets, rec
     torch.cuda.empty_cache()
     return out
@@ -748,7 +777,9 @@ def main():
         warm = args.warmup if args.only == "snapshots" else max(2, args.warmup // 4)
         paths["prefill_snapshots_draft16_gda"] = r = bench_prefill_snapshots(torch, lib, steps, warm)
         log(f"  chunked {r['chunked']['us_per_launch']:.1f} us ({r['chunked']['achieved_gbs']:.0f} GB/s), "
-            f"recurrent {r['recurrent']['us_per_launch']:.1f} us ({r['recurrent']['achieved_gbs']:.0f} GB/s)")
+            f"recurrent {r['recurrent']['us_per_launch']:.1f} us ({r['recurrent']['achieved_gbs']:.0f} GB/s); "
+            f"rollback then chunked {r['rollback_then_chunked']['us_per_launch']:.1f} us, "
+            f"fused {r['rollback_fused_into_chunked']['us_per_launch']:.1f} us")
     if dec is None:
         print(json.dumps({"partial_run": args.only, "paths": paths}), flush=True)
         return

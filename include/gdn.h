@@ -299,6 +299,33 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The rollback of the previous draft fused into a chunked prefill with
+ * snapshots: the results of gdn_rollback_select(accepted) followed by
+ * gdn_prefill_chunked_ex on the same state (koboldcpp commit log, tag
+ * v1.113.1, bullets "llama: allow partial seq_rm for GDN models for
+ * speculative decoding" and "metal: add GDN partial rollback": the accepted
+ * intermediate state becomes the input of the next step).  For each
+ * sequence b with a = accepted[b] in 1..K-1, every head reads its input
+ * state from slot a and also copies it to slot 0, bit for bit; a == 0 reads
+ * slot 0; an index outside 0..K-1 sets *err_flag (a device int32 the caller
+ * zeroes; may be NULL) and the sequence starts from slot 0.  Then slots
+ * 1..min(T, K-1), o and final_state are written as by
+ * gdn_prefill_chunked_ex.  Every other argument, layout, limit and error as
+ * there, plus accepted (device int32 [B]; NULL with B > 0 -> GDN_ERR_NULL);
+ * nothing is launched when a check fails.  The results are bit-identical to
+ * the two calls.  With T = 0 or K = 1 the entry point makes the two calls
+ * itself.
+ */
+int gdn_prefill_chunked_ex_after_rollback(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                          int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                          int32_t qkv_dtype, int32_t gate, int32_t K,
+                                          const int32_t* accepted, const void* q, const void* k,
+                                          const void* v, const float* g, const float* beta,
+                                          float* state, float* final_state, float* o,
+                                          void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                          void* stream);
+
+/*
  * The variable-length prefill of gdn_prefill_chunked_varlen with the gate
  * kind and input type of gdn_prefill_chunked_ex (the same pages' bullets):
  * qkv_dtype GDN_BF16 or GDN_F32, gate GDN_GATE_HEAD (g [total_T,H]) or

@@ -14,8 +14,8 @@ Entry points (same names as the C ABI):
   gdn_prefill_varlen_workspace_size, gdn_prefill_chunked_varlen,
   gdn_prefill_chunked_snapshots, gdn_prefill_kda_workspace_size,
   gdn_prefill_chunked_kda, gdn_prefill_workspace_size_ex, gdn_prefill_chunked_ex,
-  gdn_prefill_chunked_ex_noalloc, gdn_prefill_varlen_workspace_size_ex,
-  gdn_prefill_chunked_varlen_ex
+  gdn_prefill_chunked_ex_after_rollback, gdn_prefill_chunked_ex_noalloc,
+  gdn_prefill_varlen_workspace_size_ex, gdn_prefill_chunked_varlen_ex
 """
 
 from ._binding import (  # noqa: F401
@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     gdn_prefill_chunked,
     gdn_prefill_chunked_qk_broadcast,
     gdn_prefill_chunked_ex,
+    gdn_prefill_chunked_ex_after_rollback,
     gdn_prefill_chunked_ex_noalloc,
     gdn_prefill_chunked_kda,
     gdn_prefill_chunked_snapshots,

@@ -32,6 +32,7 @@ EXPORTED = (
     "gdn_prefill_chunked_kda",
     "gdn_prefill_workspace_size_ex",
     "gdn_prefill_chunked_ex",
+    "gdn_prefill_chunked_ex_after_rollback",
     "gdn_prefill_chunked_ex_noalloc",
     "gdn_prefill_varlen_workspace_size_ex",
     "gdn_prefill_chunked_varlen_ex",
@@ -89,6 +90,8 @@ def library() -> ctypes.CDLL:
     lib.gdn_prefill_workspace_size_ex.restype = sz
     lib.gdn_prefill_chunked_ex.argtypes = [i32] * 11 + [vp] * 9 + [sz, vp]
     lib.gdn_prefill_chunked_ex.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_ex_after_rollback.argtypes = [i32] * 11 + [vp] * 10 + [sz, vp, vp]
+    lib.gdn_prefill_chunked_ex_after_rollback.restype = ctypes.c_int
     lib.gdn_prefill_chunked_ex_noalloc.argtypes = [i32] * 11 + [vp] * 9
     lib.gdn_prefill_chunked_ex_noalloc.restype = ctypes.c_int
     lib.gdn_prefill_chunked_qk_broadcast.restype = ctypes.c_int
@@ -475,6 +478,34 @@ def gdn_prefill_chunked_ex(q, k, v, g, beta, state, head_map="grouped", final_st
         _ptr(state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
         _stream_ptr(dev))
     _check("gdn_prefill_chunked_ex", st)
+    return o
+
+
+def gdn_prefill_chunked_ex_after_rollback(accepted, q, k, v, g, beta, state, head_map="grouped",
+                                          final_state=None, o=None, workspace=None, err_flag=None,
+                                          chunk: int = 64):
+    """gdn_rollback_select(accepted, state, err_flag) followed by
+    gdn_prefill_chunked_ex on state [B,H,K,d_k,d_v], the rollback fused into
+    the prefill's chain kernel; returns o."""
+    B, T, H, Hq, hm, dk, dv, dt, gate, K, o, dev = _prefill_ex_args(q, k, v, g, beta, state, head_map,
+                                                                    final_state, o)
+    if state.dim() != 5:
+        raise ValueError("state must be [B,H,K,d_k,d_v]")
+    _dev_tensor("accepted", accepted, (torch.int32,), dev)
+    _shape("accepted", accepted, (B,))
+    if err_flag is not None:
+        _dev_tensor("err_flag", err_flag, (torch.int32,), dev)
+        if err_flag.numel() < 1:
+            raise ValueError("err_flag must hold one int32")
+    need = gdn_prefill_workspace_size_ex(B, T, H, dk, dv, chunk, dt, gate)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, (torch.uint8,), dev)
+    st = library().gdn_prefill_chunked_ex_after_rollback(
+        B, T, H, Hq, hm, dk, dv, chunk, dt, gate, K, _ptr(accepted), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        _ptr(beta), _ptr(state), _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
+        _ptr(err_flag), _stream_ptr(dev))
+    _check("gdn_prefill_chunked_ex_after_rollback", st)
     return o
 
 

@@ -173,11 +173,16 @@ size_t gdn_prefill_workspace_size_ex(int32_t B, int32_t T, int32_t H, int32_t d_
     return gdn::prefill_workspace_bytes(B, T, H, d_k, d_v, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
 }
 
-int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
-                           int32_t d_k, int32_t d_v, int32_t chunk, int32_t qkv_dtype, int32_t gate,
-                           int32_t K, const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, float* state, float* final_state, float* o,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check gdn_prefill_chunked_ex makes before it launches anything.
+int check_prefill_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map, int32_t d_k,
+                     int32_t d_v, int32_t chunk, int32_t qkv_dtype, int32_t gate, int32_t K, const void* q,
+                     const void* k, const void* v, const float* g, const float* beta, const float* state,
+                     const float* final_state, const float* o, const void* workspace,
+                     size_t workspace_bytes) {
     if (B < 0 || T < 0 || H < 0 || chunk < 1 || K < 1) return GDN_ERR_SHAPE;
     const int hs = validate_heads(H, H_qk, head_map);
     if (hs != GDN_OK) return hs;
@@ -191,6 +196,23 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (gate == GDN_GATE_KEY && !aligned16(g)) ||
         !aligned16(state) || !aligned16(o) || (final_state && !aligned16(final_state)))
         return GDN_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) return GDN_OK;
+    // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
+    if (static_cast<int64_t>(T) * H * (d_k > d_v ? d_k : d_v) * 4 >= (int64_t(1) << 31))
+        return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, d_v, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return GDN_ERR_WORKSPACE;
+    return GDN_OK;
+}
+
+// gdn_prefill_chunked_ex after check_prefill_ex, with the rollback of the
+// previous draft fused into the chain when `accepted` is given (K > 1, T > 0).
+int launch_prefill_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map, int32_t d_k,
+                      int32_t d_v, int32_t qkv_dtype, int32_t gate, int32_t K, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta, float* state, float* final_state,
+                      float* o, void* workspace, const int32_t* accepted, int32_t* err_flag, void* stream) {
     if (B == 0 || H == 0) return GDN_OK;
     if (T == 0) {
         // no token: only a requested final_state copy of slot 0 remains, which
@@ -200,14 +222,6 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
                                         nullptr, nullptr, nullptr, nullptr, nullptr, state,
                                         final_state, nullptr, stream);
     }
-    // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
-    if (static_cast<int64_t>(T) * H * (d_k > d_v ? d_k : d_v) * 4 >= (int64_t(1) << 31))
-        return GDN_ERR_UNSUPPORTED;
-    const bool kda = gate == GDN_GATE_KEY, f32 = qkv_dtype == GDN_F32;
-    const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, d_v, kda, f32);
-    if (workspace == nullptr || workspace_bytes < need ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return GDN_ERR_WORKSPACE;
     gdn::PrefillArgs a;
     a.q = q;
     a.k = k;
@@ -228,9 +242,52 @@ int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_
     a.group = H / H_qk;
     a.tiled = head_map == GDN_HEADS_TILED;
     a.K = K;
-    a.kda = kda;
-    a.f32 = f32;
+    a.kda = gate == GDN_GATE_KEY;
+    a.f32 = qkv_dtype == GDN_F32;
+    a.accepted = accepted;
+    a.err_flag = err_flag;
     return check_launch(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_chunked_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head_map,
+                           int32_t d_k, int32_t d_v, int32_t chunk, int32_t qkv_dtype, int32_t gate,
+                           int32_t K, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, float* final_state, float* o,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_prefill_ex(B, T, H, H_qk, head_map, d_k, d_v, chunk, qkv_dtype, gate, K, q, k, v, g,
+                                    beta, state, final_state, o, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    return launch_prefill_ex(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                             final_state, o, workspace, nullptr, nullptr, stream);
+}
+
+int gdn_prefill_chunked_ex_after_rollback(int32_t B, int32_t T, int32_t H, int32_t H_qk,
+                                          int32_t head_map, int32_t d_k, int32_t d_v, int32_t chunk,
+                                          int32_t qkv_dtype, int32_t gate, int32_t K,
+                                          const int32_t* accepted, const void* q, const void* k,
+                                          const void* v, const float* g, const float* beta,
+                                          float* state, float* final_state, float* o,
+                                          void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                          void* stream) {
+    int st = check_prefill_ex(B, T, H, H_qk, head_map, d_k, d_v, chunk, qkv_dtype, gate, K, q, k, v, g, beta,
+                              state, final_state, o, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    if (B > 0 && !accepted) return GDN_ERR_NULL;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (T == 0 || K == 1) {
+        // no token, or a single slot (nothing to roll back; an index other
+        // than 0 is only flagged): the two calls themselves
+        st = gdn_rollback_select(B, H, K, d_k, d_v, accepted, state, err_flag, stream);
+        if (st != GDN_OK) return st;
+        return launch_prefill_ex(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                 final_state, o, workspace, nullptr, nullptr, stream);
+    }
+    return launch_prefill_ex(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                             final_state, o, workspace, accepted, err_flag, stream);
 }
 
 int gdn_prefill_chunked_snapshots(int32_t B, int32_t T, int32_t H, int32_t H_qk,

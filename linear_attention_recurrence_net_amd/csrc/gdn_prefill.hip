@@ -1056,7 +1056,8 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      const uint16_t* __restrict__ v, float* __restrict__ state,
                      float* __restrict__ o, const char* __restrict__ ws, SeqGeom geo, int H,
                      int Hqk, int group, bool tiled, int K, float* __restrict__ final_state,
-                     const void* __restrict__ k_in, const float* __restrict__ g) {
+                     const void* __restrict__ k_in, const float* __restrict__ g,
+                     const int32_t* __restrict__ accepted, int32_t* __restrict__ err_flag) {
     using L = WsL<DK, DV, KDA, F32>;
     using M = ChainLds<DK, KDA>;
     // K and Q come from the workspace's images for KDA and for float32
@@ -1119,13 +1120,36 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         float* st = state + static_cast<size_t>(bh) * K * DK * DV;
         float* fin = K == 1 ? st : (final_state ? final_state + static_cast<size_t>(bh) * DK * DV : nullptr);
         const int nsnap = K > 1 ? min(len, K - 1) : 0;
+        // the input state: slot 0, or after a rollback fused into this call
+        // the accepted slot (an invalid index is flagged, as by the rollback,
+        // and the sequence starts from slot 0)
+        int src = 0;
+        if (accepted != nullptr) {
+            const int a = accepted[b];
+            if (a >= 0 && a < K)
+                src = a;
+            else if (h == 0 && cb == 0 && w == 0 && lane == 0 && err_flag != nullptr)
+                atomicOr(err_flag, 1);
+        }
+        const float* s_in = st + static_cast<size_t>(src) * DK * DV;
         // tile mt: d_k rows SRW w + 16 mt + 4 grp + 0..3 of column `col`
         f32x4 S[SMT];
 #pragma unroll
         for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                S[mt][rr] = st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * DV + col];
+                S[mt][rr] = s_in[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * DV + col];
+        if (src != 0) {
+            // the rollback itself: slot 0 <- slot src for this wavefront's
+            // rows and this workgroup's columns (the only ones it reads or
+            // writes; the snapshot slots are written after the first chunk's
+            // third barrier)
+#pragma unroll
+            for (int mt = 0; mt < SMT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    st[static_cast<size_t>(SRW * w + 16 * mt + 4 * grp + rr) * DV + col] = S[mt][rr];
+        }
         auto publish_state = [&]() {  // bf16 state rows -> sS (B operand of K S and Q S)
 #pragma unroll
             for (int mt = 0; mt < SMT; ++mt)
@@ -1617,7 +1641,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const unsigned bh = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((prefill_chain_kernel<DK, DV, KDA, F32>), dim3(bh * (DV / 16)), dim3(kChainThreads), 0,
                        stream, q, k, v, a.state, a.o, ws, geo, a.H, a.Hqk, a.group, a.tiled, a.K,
-                       a.final_state, a.k, a.g);
+                       a.final_state, a.k, a.g, a.accepted, a.err_flag);
     return hipGetLastError();
 }
 

@@ -24,6 +24,12 @@ struct PrefillArgs {
     int K;               // state slots per (sequence, head)
     bool kda;            // g is [.., H, dk] (one log-gate per key row)
     bool f32;            // q, k, v are float32 (else bf16)
+    // Rollback of the previous draft before this call (nullptr: none; K > 1
+    // and no cu_seqlens): the input state of sequence b is slot accepted[b],
+    // also copied to slot 0; an index outside 0..K-1 sets *err_flag (if
+    // given) and the sequence starts from slot 0.
+    const int32_t* accepted = nullptr;
+    int32_t* err_flag = nullptr;
 };
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, bool kda = false, bool f32 = false);

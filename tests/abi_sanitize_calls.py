@@ -32,6 +32,7 @@ def main(path):
         "gdn_prefill_chunked_kda": ([i32] * 8 + [vp] * 8 + [sz, vp], ctypes.c_int),
         "gdn_prefill_workspace_size_ex": ([i32] * 8, sz),
         "gdn_prefill_chunked_ex": ([i32] * 11 + [vp] * 9 + [sz, vp], ctypes.c_int),
+        "gdn_prefill_chunked_ex_after_rollback": ([i32] * 11 + [vp] * 10 + [sz, vp, vp], ctypes.c_int),
         "gdn_prefill_chunked_ex_noalloc": ([i32] * 11 + [vp] * 9, ctypes.c_int),
         "gdn_prefill_varlen_workspace_size": ([i32] * 6, sz),
         "gdn_prefill_chunked_varlen": ([i32] * 8 + [vp] * 9 + [sz, vp], ctypes.c_int),
@@ -76,6 +77,14 @@ def main(path):
     expect(pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, P, need - 1, N), ERR_WS, "prefill ws short")
     huge_T = (1 << 31) // (16 * 128 * 4)
     expect(pf(1, huge_T, 16, 128, 128, 64, P, P, P, P, P, P, P, P, 1 << 40, N), ERR_UNSUP, "prefill 2^31")
+    par = lib.gdn_prefill_chunked_ex_after_rollback
+    need_ex = lib.gdn_prefill_workspace_size_ex(1, 100, 2, 128, 128, 64, 1, 0)
+    expect(par(1, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, N, P, P, P, P, P, P, N, P, P, need_ex, N, N), ERR_NULL,
+           "prefill fused accepted NULL")
+    expect(par(1, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, P, P, P, P, P, P, P, N, P, P, need_ex - 1, N, N), ERR_WS,
+           "prefill fused ws short")
+    expect(par(0, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, N, P, P, P, P, P, P, N, P, P, 0, N, N), OK,
+           "prefill fused B = 0")
     kneed = lib.gdn_prefill_kda_workspace_size(1, 100, 4, 128, 128, 64)
     pk = lib.gdn_prefill_chunked_kda
     expect(pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, ctypes.c_void_p(260), P, P, P, P, kneed, N),

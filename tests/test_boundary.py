@@ -263,6 +263,32 @@ def test_prefill_ex_validation(lib):
     assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, P, N, N, N, 0, None) == OK
 
 
+
+def test_prefill_ex_after_rollback_validation(lib):
+    # every check of gdn_prefill_chunked_ex comes first, then accepted; none launches
+    need = lib.gdn_prefill_workspace_size_ex(2, 100, 4, 128, 128, 64, 1, 0)
+    wsa = ctypes.c_void_p(4096)
+
+    def par(B=2, T=100, H=4, Hq=4, hm=0, dk=128, dv=128, chunk=64, dt=1, gate=0, K=4, acc=P, q=P, k=P, v=P,
+            g=P, beta=P, st=P, fin=N, o=P, ws=wsa, wsb=need, err=N):
+        return lib.gdn_prefill_chunked_ex_after_rollback(B, T, H, Hq, hm, dk, dv, chunk, dt, gate, K, acc, q, k, v,
+                                                         g, beta, st, fin, o, ws, wsb, err, None)
+    assert par(acc=N) == ERR_NULL
+    assert par(st=N) == ERR_NULL
+    assert par(beta=N) == ERR_NULL
+    assert par(K=0) == ERR_SHAPE
+    assert par(H=4, Hq=3) == ERR_SHAPE
+    assert par(chunk=32, acc=N) == ERR_UNSUP
+    assert par(dk=96) == ERR_UNSUP
+    assert par(dt=5) == ERR_UNSUP
+    assert par(o=ctypes.c_void_p(264)) == ERR_UNSUP
+    assert par(wsb=need - 1, acc=N) == ERR_WS
+    assert par(ws=ctypes.c_void_p(4096 + 16)) == ERR_WS
+    assert par(ws=N) == ERR_WS
+    assert par(B=0, acc=N) == OK
+    assert par(H=0) == OK
+
+
 SCRATCH_BYTES = 256 * 1024 * 1024  # GDN_PREFILL_SCRATCH_BYTES in include/gdn.h
 
 
