@@ -51,9 +51,9 @@ DECODE_TRAFFIC = {
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
     "sha256": "4fcc1fb85fb5de6845d6454b42999af9a582b3677dc849ef1981e75e7aacbc55",
-    "fetch_kib": 33266.5,       # median over 62 decode dispatches
-    "write_kib": 66085.6875,
-    "copy_fetch_kib": 32779.5,  # median over 36 copies of 64 MiB
+    "fetch_kib": 33266.5,       # median over 162 decode dispatches
+    "write_kib": 66082.8125,
+    "copy_fetch_kib": 32779.5,  # median over 98 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
 
