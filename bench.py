@@ -50,9 +50,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_recurrence_net_amd/csrc/gdn_recurrent.hip",
                 "linear_attention_recurrence_net_amd/csrc/device_common.hpp",
                 "linear_attention_recurrence_net_amd/csrc/gdn_internal.hpp"],
-    "sha256": "4fcc1fb85fb5de6845d6454b42999af9a582b3677dc849ef1981e75e7aacbc55",
-    "fetch_kib": 33266.5,       # median over 162 decode dispatches
-    "write_kib": 66082.8125,
+    "sha256": "92ab7b180b60fc2dee614c9273ee03d7a96a4ef937c173a27a5fdaab3dcbd509",
+    "fetch_kib": 33259.0,       # median over 162 decode dispatches
+    "write_kib": 66085.1875,
     "copy_fetch_kib": 32779.5,  # median over 98 copies of 64 MiB
     "copy_write_kib": 65536.0,
 }
@@ -306,6 +306,32 @@ def bench_decode_broadcast(torch, lib, steps, warmup):
     torch.cuda.empty_cache()
     return dict(workload=w["name"], bytes=nbytes, achieved_gbs=gbs, frac_of_hbm_peak=gbs / HBM_PEAK_GBS,
                 tokens_per_s=case.B * case.T / (t["us_per_launch"] * 1e-6), **t)
+
+
+SMALL_BATCHES = (1, 8)
+
+
+def bench_small_batch(torch, lib, steps, warmup):
+    """Decode (one token) and the four-token verify (K = 4) of GDA H=16 d=128
+    at small batches, whose grids fill less than one resident round and are
+    launched in column blocks."""
+    import gdn_inputs as gi
+    out = {}
+    for kind, T, K in (("decode", 1, 1), ("verify", 4, 4)):
+        for B in SMALL_BATCHES:
+            case = gi.make_case(B, T, 16, 128, K=K, gate="gda", qkv_dtype="bf16", seed=17 + B)
+            d = upload_case(torch, case)
+            sets = _rotating_sets(torch, d, case, with_state_slot0=K == 1)
+            calls = [raw_forward_call(lib, case, s, s["state"], s["o"], K=None if K == 1 else K) for s in sets]
+            t = _timing(*run_timed(torch, calls, steps, warmup), steps)
+            nbytes = recurrent_bytes(B, T, 16, 128, K, False, True)
+            gbs = nbytes / (t["us_per_launch"] * 1e-6) / 1e9
+            out[f"{kind}_B{B}"] = dict(bytes=nbytes, achieved_gbs=gbs, frac_of_hbm_peak=gbs / HBM_PEAK_GBS,
+                                       tokens_per_s=B * T / (t["us_per_launch"] * 1e-6), **t)
+            del sets, calls, d
+            torch.cuda.empty_cache()
+    out["workload"] = (f"GDA H=16 d=128 bf16 q/k/v: decode (T=1) and verify (T=4, K=4) at B in {SMALL_BATCHES}")
+    return out
 
 
 def bench_verify(torch, lib, cfg, steps, warmup):
@@ -695,7 +721,7 @@ def main():
                     help="also run 20 device copies of 64 MiB (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--only", choices=["decode", "verify", "prefill", "prefill_kda", "prefill_f32", "broadcast", "varlen",
-                             "snapshots", "all"], default="all",
+                             "snapshots", "small", "all"], default="all",
                     help="run one workload only (the JSON line then omits the others)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -744,6 +770,10 @@ def main():
         log("decode with shared q/k heads ...")
         paths["decode_qk_broadcast_gda"] = r = bench_decode_broadcast(torch, lib, args.steps, args.warmup)
         log(f"  {r['us_per_launch']:.2f} us/launch, {r['achieved_gbs']:.0f} GB/s")
+    if args.only in ("small", "all"):
+        log("small batches ...")
+        paths["small_batch_gda"] = r = bench_small_batch(torch, lib, args.steps, args.warmup)
+        log("  " + ", ".join(f"{k} {v['us_per_launch']:.2f} us" for k, v in r.items() if isinstance(v, dict)))
     if args.only in ("prefill", "all"):
         log("prefill ...")
         steps = args.steps if args.only == "prefill" else max(5, args.steps // 10)

@@ -7,14 +7,17 @@
 //
 // Work mapping (HBM-bound: one read and one write of each fp32 state tile
 // dominate the bytes):
-//  * one workgroup per (sequence, head); its WPH wavefronts split the d_k
-//    state rows into blocks of RW = d_k / WPH whole rows (all d_v columns);
-//  * inside a wavefront, lane = CG * sub + cg with CG = d_v / 4 lanes across
+//  * one workgroup per (sequence, head) -- or, when the grid would fill less
+//    than one resident round, per (sequence, head, column block) with NCB = 2
+//    or 4 blocks of CW = d_v / NCB columns (the columns of S are independent:
+//    u_j and p_j sum column j only); its WPH wavefronts split the d_k state
+//    rows into blocks of RW = d_k / WPH rows of the workgroup's columns;
+//  * inside a wavefront, lane = CG * sub + cg with CG = CW / 4 lanes across
 //    a row (4 consecutive columns each, one 128-bit access) and RS = 64 / CG
 //    row sub-groups; sub-group `sub` holds the L = RW / RS consecutive rows
 //    sub * L .. sub * L + L - 1 of the block.  One load instruction thus
-//    moves RS whole rows of 4 * d_v bytes, and a lane's k and q rows are
-//    contiguous;
+//    moves RS row pieces of 4 * CW bytes (whole 128-byte lines at least),
+//    and a lane's k and q rows are contiguous;
 //  * a single-token launch uses two wavefronts per head (32 rows of a
 //    128 x 128 tile per lane) while the grid fits one resident round, four
 //    beyond it; several tokens use four for 128 x 128 tiles, two otherwise.
@@ -177,8 +180,9 @@ struct TokenRaw {
 // wavefront): butterflies over lane bits log2(FROM)..5.
 template <int FROM>
 __device__ __forceinline__ float sum_subgroups(float x) {
-    static_assert(FROM == 16 || FROM == 32, "row width of 64 or 128 columns");
-    if constexpr (FROM == 16) x = add_xor16(x);
+    static_assert(FROM == 8 || FROM == 16 || FROM == 32, "rows of 32, 64 or 128 columns");
+    if constexpr (FROM == 8) x = add_xor8(x);
+    if constexpr (FROM <= 16) x = add_xor16(x);
     return add_xor32(x);
 }
 
@@ -190,7 +194,7 @@ __device__ __forceinline__ float sum_subgroups(float x) {
 // tokens, whose inputs are all loaded before the first token is computed.  Two wavefronts per SIMD are
 // requested (at most 256 registers), so a 1024-head decode grid of 2048
 // wavefronts is resident at once.
-template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB, bool ROLL>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB, bool ROLL, int NCB>
 __global__ void __launch_bounds__((WPH * kWave)) __attribute__((amdgpu_waves_per_eu(2)))
 recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  const void* __restrict__ v, const float* __restrict__ g,
@@ -199,11 +203,13 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                  int n_snap, int Hqk, int group, bool tiled, const int32_t* __restrict__ accepted,
                  int32_t* __restrict__ err_flag) {
     static_assert(!(ROLL && ONE), "a fused rollback runs on the multi-token path");
-    constexpr int CG = DV / 4;        // lanes across one state row
+    constexpr int CW = DV / NCB;      // columns of the workgroup's block
+    constexpr int CG = CW / 4;        // lanes across one state row of the block
     constexpr int RS = kWave / CG;    // row sub-groups (rows per load instruction)
     constexpr int RW = DK / WPH;      // rows per wavefront
     constexpr int L = RW / RS;        // rows per lane
-    constexpr int RED = 2 * DV + 4;   // one wavefront's partial sums in LDS: u, p, k.q
+    constexpr int RED = 2 * CW + 4;   // one wavefront's partial sums in LDS: u, p, k.q
+    static_assert(NCB >= 1 && DV % NCB == 0 && CW >= 32, "column blocks of whole 128-byte lines");
     constexpr size_t TILE = static_cast<size_t>(DK) * DV;
     static_assert(L >= 4 && L % 4 == 0 && RW % RS == 0 && DK % WPH == 0, "tiling");
     static_assert(!KDA || RW <= kWave, "KDA: each lane evaluates one key row's decay");
@@ -215,8 +221,9 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int wave = threadIdx.x >> 6;
     const int cg = lane % CG;
     const int sub = lane / CG;
-    const int bh = blockIdx.x;  // b * H + h
-    const int col0 = cg * 4;
+    const int bh = static_cast<int>(blockIdx.x) / NCB;  // b * H + h
+    const int lc0 = cg * 4;                             // first column of the lane in the block
+    const int col0 = (static_cast<int>(blockIdx.x) % NCB) * CW + lc0;
     const int row0 = wave * RW + sub * L;
     const int grow = wave * RW + lane % RW;  // key row whose decay this lane evaluates (KDA)
     const int b = bh / H;
@@ -366,21 +373,21 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
                 const float ra = add_xor32_pair(u0, u2), rb = add_xor32_pair(u1, u3);
                 const float rc = add_xor32_pair(p0, p2), rd = add_xor32_pair(p1, p3);
                 const float x = add_xor16_pair(ra, rc), y = add_xor16_pair(rb, rd);
-                *reinterpret_cast<f32x2*>(mine + (sub & 1) * DV + col0 + (sub >> 1) * 2) = f32x2{x, y};
+                *reinterpret_cast<f32x2*>(mine + (sub & 1) * CW + lc0 + (sub >> 1) * 2) = f32x2{x, y};
             } else {
-                *reinterpret_cast<f32x4*>(mine + col0) = f32x4{u0, u1, u2, u3};
-                *reinterpret_cast<f32x4*>(mine + DV + col0) = f32x4{p0, p1, p2, p3};
+                *reinterpret_cast<f32x4*>(mine + lc0) = f32x4{u0, u1, u2, u3};
+                *reinterpret_cast<f32x4*>(mine + CW + lc0) = f32x4{p0, p1, p2, p3};
             }
-            mine[2 * DV] = kq;
+            mine[2 * CW] = kq;
             lds_barrier();
-            f32x4 ut = *reinterpret_cast<const f32x4*>(buf + col0);
-            f32x4 pt = *reinterpret_cast<const f32x4*>(buf + DV + col0);
-            float kqt = buf[2 * DV];
+            f32x4 ut = *reinterpret_cast<const f32x4*>(buf + lc0);
+            f32x4 pt = *reinterpret_cast<const f32x4*>(buf + CW + lc0);
+            float kqt = buf[2 * CW];
 #pragma unroll
             for (int w = 1; w < WPH; ++w) {
-                ut += *reinterpret_cast<const f32x4*>(buf + w * RED + col0);
-                pt += *reinterpret_cast<const f32x4*>(buf + w * RED + DV + col0);
-                kqt += buf[w * RED + 2 * DV];
+                ut += *reinterpret_cast<const f32x4*>(buf + w * RED + lc0);
+                pt += *reinterpret_cast<const f32x4*>(buf + w * RED + CW + lc0);
+                kqt += buf[w * RED + 2 * CW];
             }
             u0 = ut.x; u1 = ut.y; u2 = ut.z; u3 = ut.w;
             p0 = pt.x; p1 = pt.y; p2 = pt.z; p3 = pt.w;
@@ -474,10 +481,10 @@ recurrent_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
 }
 
-template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB = 0, bool ROLL = false>
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB = 0, bool ROLL = false, int NCB = 1>
 static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH, TB, ROLL>), grid, dim3(WPH * kWave), 0, stream,
+    const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * NCB);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, KDA, BF16, ONE, WPH, TB, ROLL, NCB>), grid, dim3(WPH * kWave), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.final_state, a.o, a.T, a.H, a.K,
                        a.n_snap, a.Hqk, a.group, a.tiled, a.accepted, a.err_flag);
 }
@@ -501,6 +508,32 @@ static long resident_heads() {
     return heads;
 }
 
+// Column blocks per head: a grid that would fill less than one resident
+// round (two wavefronts per SIMD) is split into 4 or 2 blocks of whole
+// 128-byte row pieces, so that more compute units share the head's state.
+// Measured on decode GDA H=16 d=128 (one token): B=1 3.1 us against 4.7 us
+// with whole rows, B=8 4.9 against 6.0, B=16 6.8 against 8.4, B=32 (two
+// blocks) 11.8 against 12.9; at B=64 two blocks took 24.2 us against 23.1.
+template <int DK, int DV, bool KDA, bool BF16, bool ONE, int WPH, int TB = 0, bool ROLL = false>
+static void launch_cols(const RecurrentArgs& a, hipStream_t stream) {
+    const long waves = static_cast<long>(a.B) * a.H * WPH;
+    // wavefronts of one resident round; half of it for the 128 x 128 draft
+    // form, whose fused-rollback launches lost 0.2-0.8 us when column blocks
+    // filled a whole round (B=8 and 16 of H=16)
+    const long round = (TB > 0 ? 1 : 2) * resident_heads();
+    if constexpr (DV >= 128) {
+        if (4 * waves <= round) {
+            launch_recurrent_shape<DK, DV, KDA, BF16, ONE, WPH, TB, ROLL, 4>(a, stream);
+            return;
+        }
+    }
+    if (2 * waves <= round) {
+        launch_recurrent_shape<DK, DV, KDA, BF16, ONE, WPH, TB, ROLL, 2>(a, stream);
+        return;
+    }
+    launch_recurrent_shape<DK, DV, KDA, BF16, ONE, WPH, TB, ROLL, 1>(a, stream);
+}
+
 // Wavefronts per head for a requested count: KDA evaluates one key row's decay
 // per lane, so its wavefronts own at most 64 rows each.
 template <int DK, bool KDA>
@@ -513,9 +546,9 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
         constexpr int WPH = heads_split<DK, KDA>(DK == 128 && DV == 128 ? kWphMulti128 : kWphMulti);
         constexpr bool DRAFT = DK == 128 && DV == 128;
         if (DRAFT && a.T >= 1 && a.T <= kDraft)
-            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, DRAFT ? kDraft : 0, true>(a, stream);
+            launch_cols<DK, DV, KDA, BF16, false, WPH, DRAFT ? kDraft : 0, true>(a, stream);
         else
-            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, 0, true>(a, stream);
+            launch_cols<DK, DV, KDA, BF16, false, WPH, 0, true>(a, stream);
         return hipGetLastError();
     }
     if (a.T == 1 && a.n_snap == 0) {
@@ -528,7 +561,7 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
                 return hipGetLastError();
             }
         }
-        launch_recurrent_shape<DK, DV, KDA, BF16, true, heads_split<DK, KDA>(kWphOne)>(a, stream);
+        launch_cols<DK, DV, KDA, BF16, true, heads_split<DK, KDA>(kWphOne)>(a, stream);
     } else {
         // Over several tokens a 128 x 128 tile is split four ways: at two
         // wavefronts per head the prefetched inputs no longer fit in registers.
@@ -538,9 +571,9 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
         // 64 x 64 KDA verify measured 0.3-0.6 us slower that way.
         constexpr bool DRAFT = DK == 128 && DV == 128;
         if (DRAFT && a.T >= 1 && a.T <= kDraft)
-            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH, DRAFT ? kDraft : 0>(a, stream);
+            launch_cols<DK, DV, KDA, BF16, false, WPH, DRAFT ? kDraft : 0>(a, stream);
         else
-            launch_recurrent_shape<DK, DV, KDA, BF16, false, WPH>(a, stream);
+            launch_cols<DK, DV, KDA, BF16, false, WPH>(a, stream);
     }
     return hipGetLastError();
 }
