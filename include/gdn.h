@@ -35,7 +35,10 @@
  *  - All validation happens on the host before any launch.  On an error
  *    nothing is launched and no output is touched.  A launch failure is
  *    reported as GDN_ERR_HIP.  Calls are asynchronous.
- *  - Outputs must not overlap inputs; final_state must not overlap state.
+ *  - No array a call writes (o, state, final_state, the workspace,
+ *    err_flag) may share a byte with any other of its arrays; the host
+ *    checks the byte ranges the call's sizes give and returns GDN_ERR_ALIAS
+ *    (inputs may share memory with each other).
  *    NaN/Inf inputs propagate; they are not checked.
  */
 #ifndef GDN_H
@@ -56,8 +59,11 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3, /* d_k or d_v not in {64,128}, bad dtype/gate     */
     GDN_ERR_WORKSPACE = 4,   /* prefill workspace missing or too small          */
     GDN_ERR_HIP = 5,         /* the HIP runtime reported a launch error         */
-    GDN_ERR_SCRATCH = 6      /* the problem needs more than the library's fixed
+    GDN_ERR_SCRATCH = 6,     /* the problem needs more than the library's fixed
                                 scratch array (gdn_prefill_chunked_ex_noalloc)  */
+    GDN_ERR_ALIAS = 7        /* an array the call writes (o, state, final_state,
+                                workspace, err_flag) overlaps another array of
+                                the call                                        */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype; /* dtype of q, k, v only */

@@ -17,6 +17,50 @@ bool supported_head(int d_k, int d_v) { return head_size(d_k) && head_size(d_v);
 
 int check_launch(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// The bytes [p, p + n) of one array of a call; `out` if the call writes it.
+struct Span {
+    const void* p;
+    size_t n;
+    bool out;
+};
+
+// GDN_ERR_ALIAS if an array the call writes shares a byte with any other of
+// its arrays (inputs may share memory with each other); NULL or empty arrays
+// take no part.
+int check_disjoint(const Span* s, int n) {
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j) {
+            if (!(s[i].out || s[j].out) || !s[i].p || !s[j].p || s[i].n == 0 || s[j].n == 0) continue;
+            const uintptr_t a = reinterpret_cast<uintptr_t>(s[i].p), b = reinterpret_cast<uintptr_t>(s[j].p);
+            if (a < b + s[j].n && b < a + s[i].n) return GDN_ERR_ALIAS;
+        }
+    return GDN_OK;
+}
+
+// The arrays of a token-kernel call (q, k [B,T,H_qk,d_k]; v, o [B,T,H,d_v];
+// g, beta; the K-slot state and the final state), plus the accepted lengths
+// and the error flag of a fused rollback.
+int check_recurrent_disjoint(int B, int T, int H, int H_qk, int d_k, int d_v, int qkv_dtype, int gate,
+                             int K, const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, const void* state, const void* final_state, const void* o,
+                             const void* accepted = nullptr, const void* err_flag = nullptr) {
+    const size_t bt = static_cast<size_t>(B) * T, e = qkv_dtype == GDN_BF16 ? 2 : 4;
+    const size_t tile = static_cast<size_t>(d_k) * d_v * 4;
+    const Span s[] = {
+        {q, bt * H_qk * d_k * e, false},
+        {k, bt * H_qk * d_k * e, false},
+        {v, bt * H * d_v * e, false},
+        {g, bt * H * (gate == GDN_GATE_KEY ? d_k : 1) * 4, false},
+        {beta, bt * H * 4, false},
+        {accepted, static_cast<size_t>(B) * 4, false},
+        {o, bt * H * d_v * 4, true},
+        {state, static_cast<size_t>(B) * H * K * tile, true},
+        {final_state, static_cast<size_t>(B) * H * tile, true},
+        {err_flag, 4, true},
+    };
+    return check_disjoint(s, sizeof(s) / sizeof(s[0]));
+}
+
 // H value heads read H_qk query/key heads (H a multiple of H_qk).
 int validate_heads(int H, int H_qk, int head_map) {
     if (H_qk < 1 || (H > 0 && H % H_qk != 0)) return GDN_ERR_SHAPE;
@@ -62,6 +106,9 @@ int gdn_forward_qk_broadcast(int32_t B, int32_t T, int32_t H, int32_t H_qk, int3
     st = validate_heads(H, H_qk, head_map);
     if (st != GDN_OK) return st;
     if (B == 0 || H == 0) return GDN_OK;
+    st = check_recurrent_disjoint(B, T, H, H_qk, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                  final_state, o);
+    if (st != GDN_OK) return st;
     // With no token, nothing changes unless a final_state copy is requested.
     if (T == 0 && final_state == nullptr) return GDN_OK;
     return launch_forward(B, T, H, H_qk, head_map, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
@@ -82,6 +129,9 @@ int gdn_forward_snapshots_after_rollback(int32_t B, int32_t T, int32_t H, int32_
     if (st != GDN_OK) return st;
     if (B > 0 && !accepted) return GDN_ERR_NULL;
     if (B == 0 || H == 0) return GDN_OK;
+    st = check_recurrent_disjoint(B, T, H, H_qk, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                  final_state, o, accepted, err_flag);
+    if (st != GDN_OK) return st;
     if (T == 0 || K == 1) {
         // no token, or a single slot (nothing to roll back; an index other
         // than 0 is only flagged): the two calls themselves
@@ -155,6 +205,11 @@ int gdn_rollback_select(int32_t B, int32_t H, int32_t K, int32_t d_k, int32_t d_
     const size_t tile = static_cast<size_t>(d_k) * static_cast<size_t>(d_v);
     if (tile % 4 != 0 || !aligned16(state)) return GDN_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return GDN_OK;
+    const Span s[] = {{accepted, static_cast<size_t>(B) * 4, false},
+                      {state, static_cast<size_t>(B) * H * K * tile * 4, true},
+                      {err_flag, 4, true}};
+    const int st = check_disjoint(s, 3);
+    if (st != GDN_OK) return st;
     return check_launch(gdn::launch_rollback(B, H, K, tile, accepted, state, err_flag,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -196,11 +251,31 @@ int check_prefill_ex(int32_t B, int32_t T, int32_t H, int32_t H_qk, int32_t head
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (gate == GDN_GATE_KEY && !aligned16(g)) ||
         !aligned16(state) || !aligned16(o) || (final_state && !aligned16(final_state)))
         return GDN_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || T == 0) return GDN_OK;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (T == 0)
+        return check_recurrent_disjoint(B, T, H, H_qk, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                        K > 1 ? final_state : nullptr, o);
     // the kernels address one sequence's [T,H,d] rows with 32-bit byte offsets
     if (static_cast<int64_t>(T) * H * (d_k > d_v ? d_k : d_v) * 4 >= (int64_t(1) << 31))
         return GDN_ERR_UNSUPPORTED;
     const size_t need = gdn::prefill_workspace_bytes(B, T, H, d_k, d_v, gate == GDN_GATE_KEY, qkv_dtype == GDN_F32);
+    {
+        // the workspace bytes the kernels write, against every other array
+        const size_t bt = static_cast<size_t>(B) * T, e = qkv_dtype == GDN_BF16 ? 2 : 4;
+        const Span s[] = {
+            {workspace, need, true},
+            {q, bt * H_qk * d_k * e, false},
+            {k, bt * H_qk * d_k * e, false},
+            {v, bt * H * d_v * e, false},
+            {g, bt * H * (gate == GDN_GATE_KEY ? d_k : 1) * 4, false},
+            {beta, bt * H * 4, false},
+            {o, bt * H * d_v * 4, true},
+            {state, static_cast<size_t>(B) * H * K * d_k * d_v * 4, true},
+            {K > 1 ? final_state : nullptr, static_cast<size_t>(B) * H * d_k * d_v * 4, true},
+        };
+        const int st = check_disjoint(s, sizeof(s) / sizeof(s[0]));
+        if (st != GDN_OK) return st;
+    }
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_WORKSPACE;
@@ -273,11 +348,14 @@ int gdn_prefill_chunked_ex_after_rollback(int32_t B, int32_t T, int32_t H, int32
                                           float* state, float* final_state, float* o,
                                           void* workspace, size_t workspace_bytes, int32_t* err_flag,
                                           void* stream) {
+    if (B > 0 && !accepted) return GDN_ERR_NULL;
     int st = check_prefill_ex(B, T, H, H_qk, head_map, d_k, d_v, chunk, qkv_dtype, gate, K, q, k, v, g, beta,
                               state, final_state, o, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
-    if (B > 0 && !accepted) return GDN_ERR_NULL;
     if (B == 0 || H == 0) return GDN_OK;
+    st = check_recurrent_disjoint(B, T, H, H_qk, d_k, d_v, qkv_dtype, gate, K, q, k, v, g, beta, state,
+                                  K > 1 ? final_state : nullptr, o, accepted, err_flag);
+    if (st != GDN_OK) return st;
     if (T == 0 || K == 1) {
         // no token, or a single slot (nothing to roll back; an index other
         // than 0 is only flagged): the two calls themselves
@@ -352,6 +430,22 @@ int gdn_prefill_chunked_varlen_ex(int32_t N, int32_t total_T, int32_t H, int32_t
         return GDN_ERR_UNSUPPORTED;
     const bool kda = gate == GDN_GATE_KEY, f32 = qkv_dtype == GDN_F32;
     const size_t need = gdn::prefill_varlen_workspace_bytes(N, total_T, H, d_k, d_v, kda, f32);
+    {
+        const size_t t = static_cast<size_t>(total_T), e = f32 ? 4 : 2;
+        const Span s[] = {
+            {cu_seqlens, (static_cast<size_t>(N) + 1) * 4, false},
+            {q, t * H_qk * d_k * e, false},
+            {k, t * H_qk * d_k * e, false},
+            {v, t * H * d_v * e, false},
+            {g, t * H * (kda ? d_k : 1) * 4, false},
+            {beta, t * H * 4, false},
+            {o, t * H * d_v * 4, true},
+            {state, static_cast<size_t>(N) * H * d_k * d_v * 4, true},
+            {workspace, need, true},
+        };
+        const int st = check_disjoint(s, sizeof(s) / sizeof(s[0]));
+        if (st != GDN_OK) return st;
+    }
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_WORKSPACE;
@@ -424,6 +518,7 @@ const char* gdn_status_str(int status) {
         case GDN_ERR_HIP: return "HIP runtime error at launch";
         case GDN_ERR_SCRATCH:
             return "prefill workspace exceeds the library's fixed scratch array (GDN_PREFILL_SCRATCH_BYTES)";
+        case GDN_ERR_ALIAS: return "an array the call writes overlaps another of its arrays";
         default: return "unknown status";
     }
 }

@@ -6,8 +6,9 @@ python abi_sanitize_calls.py <path to a sanitized libgdn.so>."""
 import ctypes
 import sys
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH, ERR_ALIAS = range(8)
 P = ctypes.c_void_p(256)  # a fake, 16-byte aligned "device" pointer: never dereferenced
+D = [ctypes.c_void_p((i + 1) << 40) for i in range(24)]  # distinct fake pointers, 1 TiB apart
 N = None
 SCRATCH_BYTES = 256 * 1024 * 1024
 
@@ -74,14 +75,14 @@ def main(path):
     expect(lib.gdn_prefill_workspace_size(1, 100, 2, 128, 128, 32), 0, "workspace size chunk 32")
     pf = lib.gdn_prefill_chunked
     expect(pf(1, 100, 2, 128, 128, 64, N, P, P, P, P, P, P, P, need, N), ERR_NULL, "prefill q NULL")
-    expect(pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, P, need - 1, N), ERR_WS, "prefill ws short")
+    expect(pf(1, 100, 2, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], need - 1, N), ERR_WS, "prefill ws short")
     huge_T = (1 << 31) // (16 * 128 * 4)
     expect(pf(1, huge_T, 16, 128, 128, 64, P, P, P, P, P, P, P, P, 1 << 40, N), ERR_UNSUP, "prefill 2^31")
     par = lib.gdn_prefill_chunked_ex_after_rollback
     need_ex = lib.gdn_prefill_workspace_size_ex(1, 100, 2, 128, 128, 64, 1, 0)
     expect(par(1, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, N, P, P, P, P, P, P, N, P, P, need_ex, N, N), ERR_NULL,
            "prefill fused accepted NULL")
-    expect(par(1, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, P, P, P, P, P, P, P, N, P, P, need_ex - 1, N, N), ERR_WS,
+    expect(par(1, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, D[7], D[8], need_ex - 1, N, N), ERR_WS,
            "prefill fused ws short")
     expect(par(0, 100, 2, 2, 0, 128, 128, 64, 1, 0, 4, N, P, P, P, P, P, P, N, P, P, 0, N, N), OK,
            "prefill fused B = 0")
@@ -95,21 +96,21 @@ def main(path):
     pe = lib.gdn_prefill_chunked_ex
     expect(pe(1, 100, 4, 4, 0, 128, 128, 64, 5, 0, 1, P, P, P, P, P, P, N, P, P, 1 << 30, N), ERR_UNSUP, "ex dtype")
     kf = wsx(1, 100, 4, 128, 128, 64, 0, 1)
-    expect(pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, P, P, P, P, P, P, N, P, P, kf - 1, N), ERR_WS, "ex ws short")
+    expect(pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, D[0], D[1], D[2], D[3], D[4], D[5], N, D[6], D[7], kf - 1, N), ERR_WS, "ex ws short")
     pn = lib.gdn_prefill_chunked_ex_noalloc
     n = SCRATCH_BYTES // wsx(1, 64, 1, 128, 128, 64, 1, 0)
-    expect(pn(1, 64 * n + 1, 1, 1, 0, 128, 128, 64, 1, 0, 1, P, P, P, P, P, P, N, P, N), ERR_SCRATCH,
+    expect(pn(1, 64 * n + 1, 1, 1, 0, 128, 128, 64, 1, 0, 1, D[0], D[1], D[2], D[3], D[4], D[5], N, D[6], N), ERR_SCRATCH,
            "noalloc beyond the scratch array")
     expect(pn(1, 0, 4, 4, 0, 128, 128, 64, 1, 0, 1, N, N, N, N, N, P, N, N, N), OK, "noalloc T = 0")
     vneed = lib.gdn_prefill_varlen_workspace_size(3, 300, 4, 128, 128, 64)
     pv = lib.gdn_prefill_chunked_varlen
     expect(pv(3, 300, 4, 2, 0, 128, 128, 64, N, P, P, P, P, P, P, P, P, vneed, N), ERR_NULL, "varlen cu NULL")
-    expect(pv(3, 300, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, vneed - 1, N), ERR_WS, "varlen ws")
+    expect(pv(3, 300, 4, 2, 0, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], D[8], vneed - 1, N), ERR_WS, "varlen ws")
     vx = lib.gdn_prefill_varlen_workspace_size_ex(3, 300, 4, 128, 128, 64, 0, 1)
     pvx = lib.gdn_prefill_chunked_varlen_ex
-    expect(pvx(3, 300, 4, 2, 0, 128, 128, 64, 0, 1, P, P, P, P, P, P, P, P, P, vx - 1, N), ERR_WS, "varlen ex ws")
+    expect(pvx(3, 300, 4, 2, 0, 128, 128, 64, 0, 1, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], D[8], vx - 1, N), ERR_WS, "varlen ex ws")
     expect(pvx(3, 300, 4, 2, 0, 128, 128, 64, 0, 3, P, P, P, P, P, P, P, P, P, vx, N), ERR_UNSUP, "varlen ex gate")
-    for s in list(range(7)) + [99]:
+    for s in list(range(8)) + [99]:
         expect(bool(lib.gdn_status_str(s)), True, f"status string {s}")
     bad = [c for c in checks if not c[0]]
     for _, what, got, want in bad:

@@ -23,7 +23,7 @@ from linear_attention_recurrence_net_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH, ERR_ALIAS = range(8)
 
 
 def _declared_functions():
@@ -48,13 +48,16 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.gdn_status_str(s)
     assert b"unknown" in lib.gdn_status_str(99)
 
 
 P = ctypes.c_void_p(256)  # a fake, 16-byte aligned "device" pointer: never dereferenced
 N = None
+# distinct fake pointers, 1 TiB apart and 256-byte aligned (never dereferenced),
+# for calls that must get past the check that written arrays overlap no other
+D = [ctypes.c_void_p((i + 1) << 40) for i in range(24)]
 
 
 def fwd(lib, B=1, T=1, H=1, dk=64, dv=64, dt=1, gate=0, q=P, k=P, v=P, g=P, beta=P, st=P, o=P):
@@ -135,14 +138,14 @@ def test_prefill_validation(lib):
     assert pf(1, 100, 2, 128, 128, 32, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
     assert pf(1, 100, 2, 96, 96, 64, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
     small = ws(1, 100, 2, 128, 128, 64)
-    assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, N, small, None) == ERR_WS
-    assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, P, small - 1, None) == ERR_WS
-    assert pf(1, 100, 2, 128, 128, 64, P, P, P, P, P, P, P, ctypes.c_void_p(272), small, None) == ERR_WS
-    assert pf(1, 0, 2, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == OK
+    assert pf(1, 100, 2, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, small, None) == ERR_WS
+    assert pf(1, 100, 2, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], small - 1, None) == ERR_WS
+    assert pf(1, 100, 2, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], ctypes.c_void_p(272), small, None) == ERR_WS
+    assert pf(1, 0, 2, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, 0, None) == OK
     # one sequence's [T,H,d] fp32 rows must stay below 2^31 bytes
     huge_T = (1 << 31) // (16 * 128 * 4)
     assert pf(1, huge_T, 16, 128, 128, 64, P, P, P, P, P, P, P, P, 1 << 40, None) == ERR_UNSUP
-    assert pf(1, huge_T - 1, 16, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == ERR_WS
+    assert pf(1, huge_T - 1, 16, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, 0, None) == ERR_WS
 
 
 def test_workspace_grows_with_tokens(lib):
@@ -172,8 +175,8 @@ def test_qk_broadcast_validation(lib):
     # B, T, H, H_qk, head_map, dk, dv, chunk, q, k, v, g, beta, state, o, ws, ws_bytes, stream
     assert pb(1, 100, 4, 3, 0, 128, 128, 64, P, P, P, P, P, P, P, P, big, None) == ERR_SHAPE
     assert pb(1, 100, 4, 2, 5, 128, 128, 64, P, P, P, P, P, P, P, P, big, None) == ERR_UNSUP
-    assert pb(1, 100, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, N, big, None) == ERR_WS
-    assert pb(1, 0, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, N, 0, None) == OK
+    assert pb(1, 100, 4, 2, 0, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, big, None) == ERR_WS
+    assert pb(1, 0, 4, 2, 0, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, 0, None) == OK
 
 
 def test_prefill_varlen_validation(lib):
@@ -187,8 +190,8 @@ def test_prefill_varlen_validation(lib):
     assert pv(-1, 300, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
     assert pv(3, 300, 4, 3, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need, None) == ERR_SHAPE
     assert pv(3, 300, 4, 2, 0, 128, 128, 32, P, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
-    assert pv(3, 300, 4, 2, 0, 128, 128, 64, P, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
-    assert pv(0, 300, 4, 2, 0, 128, 128, 64, N, P, P, P, P, P, P, P, N, 0, None) == OK
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], D[8], need - 1, None) == ERR_WS
+    assert pv(0, 300, 4, 2, 0, 128, 128, 64, N, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, 0, None) == OK
     assert pv(3, 0, 4, 2, 0, 128, 128, 64, P, N, N, N, N, N, P, N, N, 0, None) == OK
 
 
@@ -208,9 +211,9 @@ def test_prefill_varlen_ex_validation(lib):
     assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 2, P, P, P, P, P, P, P, P, P, kda, None) == ERR_UNSUP
     g8 = ctypes.c_void_p(264)  # 8-byte aligned: fine for GDA gates, not for KDA's 16-byte pieces
     assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, P, P, P, P, g8, P, P, P, P, kda, None) == ERR_UNSUP
-    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, P, P, P, P, P, P, P, P, P, kda - 1, None) == ERR_WS
-    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 0, 0, P, P, P, P, P, P, P, P, P, f32 - 1, None) == ERR_WS
-    assert pv(0, 300, 4, 2, 0, 128, 128, 64, 1, 1, N, P, P, P, P, P, P, P, N, 0, None) == OK
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 1, 1, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], D[8], kda - 1, None) == ERR_WS
+    assert pv(3, 300, 4, 2, 0, 128, 128, 64, 0, 0, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], D[8], f32 - 1, None) == ERR_WS
+    assert pv(0, 300, 4, 2, 0, 128, 128, 64, 1, 1, N, D[0], D[1], D[2], D[3], D[4], D[5], D[6], N, 0, None) == OK
 
 
 def test_prefill_snapshots_validation(lib):
@@ -222,7 +225,7 @@ def test_prefill_snapshots_validation(lib):
     assert ps(2, 100, 4, 4, 0, 128, 128, 64, 4, P, P, P, P, P, N, P, P, P, need, None) == ERR_NULL
     assert ps(2, 100, 4, 4, 0, 128, 96, 64, 4, P, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
     assert ps(2, 100, 4, 4, 2, 128, 128, 64, 4, P, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
-    assert ps(2, 100, 4, 4, 0, 128, 128, 64, 4, P, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
+    assert ps(2, 100, 4, 4, 0, 128, 128, 64, 4, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], D[8], need - 1, None) == ERR_WS
     # empty problems launch nothing; T = 0 without final_state (or with K = 1) is a no-op
     assert ps(0, 100, 4, 4, 0, 128, 128, 64, 4, N, N, N, N, N, N, N, N, N, 0, None) == OK
     assert ps(2, 0, 4, 4, 0, 128, 128, 64, 4, N, N, N, N, N, P, N, N, N, 0, None) == OK
@@ -241,8 +244,8 @@ def test_prefill_kda_validation(lib):
     assert pk(1, 100, 4, 4, 0, 128, 128, 16, P, P, P, P, P, P, P, P, need, None) == ERR_UNSUP
     assert pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, ctypes.c_void_p(260), P, P, P, P, need,
               None) == ERR_UNSUP
-    assert pk(1, 100, 4, 4, 0, 128, 128, 64, P, P, P, P, P, P, P, P, need - 1, None) == ERR_WS
-    assert pk(1, 0, 4, 4, 0, 128, 128, 64, N, N, N, N, N, P, N, N, 0, None) == OK
+    assert pk(1, 100, 4, 4, 0, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7], need - 1, None) == ERR_WS
+    assert pk(1, 0, 4, 4, 0, 128, 128, 64, N, N, N, N, N, D[0], N, N, 0, None) == OK
 
 
 def test_prefill_ex_validation(lib):
@@ -257,20 +260,20 @@ def test_prefill_ex_validation(lib):
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 0, P, P, P, P, P, P, N, P, P, gda_f, None) == ERR_SHAPE
     assert pe(1, 100, 4, 4, 0, 128, 128, 64, 5, 0, 1, P, P, P, P, P, P, N, P, P, gda_f, None) == ERR_UNSUP
     # KDA with K > 1 snapshot slots is accepted up to the workspace check
-    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, P, P, P, P, P, P, N, P, P, kda_bf - 1, None) == ERR_WS
-    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 1, P, P, P, P, P, P, N, P, P, gda_f - 1, None) == ERR_WS
-    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, P, P, P, P, P, P, N, P, P, kda_f - 1, None) == ERR_WS
-    assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, P, N, N, N, 0, None) == OK
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 1, 1, 2, D[0], D[1], D[2], D[3], D[4], D[5], N, D[6], D[7], kda_bf - 1, None) == ERR_WS
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 0, 1, D[0], D[1], D[2], D[3], D[4], D[5], N, D[6], D[7], gda_f - 1, None) == ERR_WS
+    assert pe(1, 100, 4, 4, 0, 128, 128, 64, 0, 1, 1, D[0], D[1], D[2], D[3], D[4], D[5], N, D[6], D[7], kda_f - 1, None) == ERR_WS
+    assert pe(1, 0, 4, 4, 0, 128, 128, 64, 0, 0, 1, N, N, N, N, N, D[0], N, N, N, 0, None) == OK
 
 
 
 def test_prefill_ex_after_rollback_validation(lib):
-    # every check of gdn_prefill_chunked_ex comes first, then accepted; none launches
+    # accepted first, then every check of gdn_prefill_chunked_ex; none launches
     need = lib.gdn_prefill_workspace_size_ex(2, 100, 4, 128, 128, 64, 1, 0)
     wsa = ctypes.c_void_p(4096)
 
-    def par(B=2, T=100, H=4, Hq=4, hm=0, dk=128, dv=128, chunk=64, dt=1, gate=0, K=4, acc=P, q=P, k=P, v=P,
-            g=P, beta=P, st=P, fin=N, o=P, ws=wsa, wsb=need, err=N):
+    def par(B=2, T=100, H=4, Hq=4, hm=0, dk=128, dv=128, chunk=64, dt=1, gate=0, K=4, acc=D[0], q=D[1], k=D[2],
+            v=D[3], g=D[4], beta=D[5], st=D[6], fin=N, o=D[7], ws=wsa, wsb=need, err=N):
         return lib.gdn_prefill_chunked_ex_after_rollback(B, T, H, Hq, hm, dk, dv, chunk, dt, gate, K, acc, q, k, v,
                                                          g, beta, st, fin, o, ws, wsb, err, None)
     assert par(acc=N) == ERR_NULL
@@ -278,15 +281,47 @@ def test_prefill_ex_after_rollback_validation(lib):
     assert par(beta=N) == ERR_NULL
     assert par(K=0) == ERR_SHAPE
     assert par(H=4, Hq=3) == ERR_SHAPE
-    assert par(chunk=32, acc=N) == ERR_UNSUP
+    assert par(chunk=32) == ERR_UNSUP
     assert par(dk=96) == ERR_UNSUP
     assert par(dt=5) == ERR_UNSUP
     assert par(o=ctypes.c_void_p(264)) == ERR_UNSUP
-    assert par(wsb=need - 1, acc=N) == ERR_WS
+    assert par(wsb=need - 1) == ERR_WS
+    assert par(o=D[1]) == ERR_ALIAS      # o is q
+    assert par(err=D[6]) == ERR_ALIAS    # the error flag inside the state
+    assert par(acc=D[7]) == ERR_ALIAS    # the accepted lengths inside o
     assert par(ws=ctypes.c_void_p(4096 + 16)) == ERR_WS
     assert par(ws=N) == ERR_WS
     assert par(B=0, acc=N) == OK
     assert par(H=0) == OK
+
+
+
+def test_overlapping_arrays_are_refused(lib):
+    """An array the call writes may share no byte with another of its arrays:
+    GDN_ERR_ALIAS, before any launch.  Inputs may share memory."""
+    at = lambda p, off: ctypes.c_void_p(p.value + off)
+    # decode, bf16, B=T=H=1, d=64: q, k, v are 128 bytes each
+    fw = lambda q, k, v, g, b, st, o: lib.gdn_forward(1, 1, 1, 64, 64, 1, 0, q, k, v, g, b, st, o, None)
+    assert fw(D[0], D[1], D[2], D[3], D[4], D[5], D[0]) == ERR_ALIAS             # o is q
+    assert fw(D[0], D[1], D[2], D[3], D[4], at(D[2], 112), D[6]) == ERR_ALIAS    # state begins in v
+    assert fw(D[0], D[1], D[2], D[3], D[4], D[5], at(D[5], 16368)) == ERR_ALIAS  # o ends the state
+    # snapshots: the final state inside slot 3 of the state (K = 4 slots of 16 KiB)
+    assert lib.gdn_forward_snapshots(1, 1, 1, 64, 64, 1, 0, 4, D[0], D[1], D[2], D[3], D[4], D[5],
+                                     at(D[5], 3 * 16384), D[6], None) == ERR_ALIAS
+    # rollback: the error flag in the last slot
+    assert lib.gdn_rollback_select(2, 2, 4, 64, 64, D[0], D[1], at(D[1], 2 * 2 * 4 * 16384 - 4), None) == ERR_ALIAS
+    # prefill: q (100 tokens x 2 heads x 128 bf16 = 51200 bytes) followed at once by o is fine
+    # (the next check, a missing workspace, fails), one 16-byte piece earlier it is not
+    pe = lambda o, ws, wsb: lib.gdn_prefill_chunked_ex(1, 100, 2, 2, 0, 128, 128, 64, 1, 0, 1, D[0], D[1], D[2],
+                                                      D[3], D[4], D[5], N, o, ws, wsb, None)
+    need = lib.gdn_prefill_workspace_size_ex(1, 100, 2, 128, 128, 64, 1, 0)
+    assert pe(at(D[0], 51200), N, 0) == ERR_WS
+    assert pe(at(D[0], 51200 - 16), N, 0) == ERR_ALIAS
+    assert pe(D[6], at(D[6], 256), need) == ERR_ALIAS  # the workspace inside o
+    assert pe(D[6], at(D[5], -(need - 256)), need) == ERR_ALIAS  # the workspace runs into the state
+    # variable-length prefill: o over the sequence offsets
+    assert lib.gdn_prefill_chunked_varlen(2, 100, 2, 2, 0, 128, 128, 64, D[0], D[1], D[2], D[3], D[4], D[5],
+                                          D[6], at(D[0], 0), D[7], 1 << 30, None) == ERR_ALIAS
 
 
 SCRATCH_BYTES = 256 * 1024 * 1024  # GDN_PREFILL_SCRATCH_BYTES in include/gdn.h
@@ -314,7 +349,7 @@ def test_prefill_ex_noalloc_validation(lib):
         assert wsz(1, 64 * n, 1, 128, 128, 64, dt, gate) <= SCRATCH_BYTES
         assert wsz(1, 64 * n + 1, 1, 128, 128, 64, dt, gate) > SCRATCH_BYTES
         assert pn(1, 64 * n + 1, 1, 1, 0, 128, 128, 64, dt, gate, 1,
-                  P, P, P, P, P, P, N, P, None) == ERR_SCRATCH
+                  D[10], D[11], D[12], D[13], D[14], D[15], N, D[16], None) == ERR_SCRATCH
 
 
 def test_bench_runs_on_one_gpu_only():
