@@ -40,6 +40,10 @@ struct RecurrentArgs {
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 
+// Compute units of the current device (read once per device; 256 if the
+// runtime cannot say).
+int cu_count();
+
 hipError_t launch_rollback(int B, int H, int K, size_t tile_elems, const int32_t* accepted,
                            float* state, int32_t* err_flag, hipStream_t stream);
 

@@ -475,7 +475,7 @@ __device__ __forceinline__ void store_v_image(const void* v, char* wsb, size_t t
     }
 }
 
-template <int DK, int DV, bool F32>
+template <int DK, int DV, bool F32, bool SPLIT>
 __global__ void __launch_bounds__(64)
 prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     const void* __restrict__ v, const float* __restrict__ g,
@@ -490,7 +490,12 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
     __shared__ __attribute__((aligned(16))) float sBeta[kC];
 
     const int lane = threadIdx.x;
-    const int blk = blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
+    // SPLIT: two blocks per chunk, the first forming A, T1, the gate block
+    // and (float32 inputs) the K and V images, the second QKm and the Q
+    // image; each output takes the same instructions as in the single block
+    const int blk = SPLIT ? blockIdx.x >> 1 : blockIdx.x;  // h * CT + c: workspace block of head h, chunk c
+    const bool doA = !SPLIT || (blockIdx.x & 1) == 0;
+    const bool doQ = !SPLIT || (blockIdx.x & 1) == 1;
     const int h = blk / geo.CT;
     const int c = blk - h * geo.CT;
     const int i = geo.owner(c);
@@ -520,7 +525,7 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
     sG[lane] = G;
     sBeta[lane] = bv;
-    {
+    if (doA) {
         float* e = reinterpret_cast<float*>(wsb + L::kE);
         const float Glast = __shfl(G, 63, 64);
         e[kEg + lane] = expf(G);
@@ -542,17 +547,20 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
             kf[t][ks] = r < nvalid ? ld8_in<F32>(k, row_at(r) + 32 * ks + 8 * grp) : zero_bf16x8();
     }
     if constexpr (F32) {  // the bf16 K and V images for the chain
+        if (doA) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                *reinterpret_cast<bf16x8*>(wsb + L::kKI + (static_cast<size_t>(16 * t + lr) * DK + 32 * ks + 8 * grp) * 2) =
-                    kf[t][ks];
-        store_v_image<L, DV>(v, wsb, t0, nvalid, H, h, lane);
+                for (int ks = 0; ks < KS; ++ks)
+                    *reinterpret_cast<bf16x8*>(wsb + L::kKI + (static_cast<size_t>(16 * t + lr) * DK + 32 * ks + 8 * grp) * 2) =
+                        kf[t][ks];
+            store_v_image<L, DV>(v, wsb, t0, nvalid, H, h, lane);
+        }
     }
     __syncthreads();
 
     // A = strict lower part of diag(beta) (exp(G_r - G_s)) o (K K^T)
+    if (doA)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -571,6 +579,7 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
         }
     }
 
+    if (doQ) {
     // fragments of the chunk's q rows (zero beyond the sequence end)
     bf16x8 qp[4][KS];
 #pragma unroll
@@ -625,6 +634,8 @@ prefill_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
                 u32x4{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
         }
     }
+    }  // doQ
+    if (!doA) return;
     __syncthreads();
 
     solve_store_t1<L>(sA, sBeta, wsb, lane);
@@ -1628,9 +1639,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     if (KDA)
         hipLaunchKernelGGL((prefill_prep_kda_kernel<DK, DV, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k,
                            a.v, a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
+    else if (prep_grid.x <= 2u * static_cast<unsigned>(cu_count()))
+        // few blocks: each block's latency sets the prep's time, so a chunk's
+        // A and T1 and its QKm go to two blocks (B=1 H=16 d=128: 64 tokens
+        // 11.4 us against 14.3 us, 256 tokens 16.0 against 19.4, 1024 tokens
+        // 33.3 against 36.5; at 4096 tokens, 1024 blocks, 98 against 95)
+        hipLaunchKernelGGL((prefill_prep_kernel<DK, DV, F32, true>), dim3(2 * prep_grid.x), dim3(64), 0, stream,
+                           a.q, a.k, a.v, a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     else
-        hipLaunchKernelGGL((prefill_prep_kernel<DK, DV, F32>), prep_grid, dim3(64), 0, stream, a.q, a.k, a.v,
-                           a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
+        hipLaunchKernelGGL((prefill_prep_kernel<DK, DV, F32, false>), prep_grid, dim3(64), 0, stream, a.q, a.k,
+                           a.v, a.g, a.beta, ws, geo, a.H, a.Hqk, a.group, a.tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // with float32 inputs the chain reads only the workspace's bf16 images

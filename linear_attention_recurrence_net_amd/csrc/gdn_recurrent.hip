@@ -489,24 +489,24 @@ static void launch_recurrent_shape(const RecurrentArgs& a, hipStream_t stream) {
                        a.n_snap, a.Hqk, a.group, a.tiled, a.accepted, a.err_flag);
 }
 
-// Heads that one round of the single-token 128 x 128 kernel holds at two
-// wavefronts per head and two wavefronts per SIMD: four per compute unit.
 // Read once per device (host threads may race to fill an entry; they all
 // store the same value).
-static long resident_heads() {
-    static std::atomic<long> cache[64];
+int cu_count() {
+    static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
-    long heads = cache[dev].load(std::memory_order_relaxed);
-    if (heads == 0) {
-        int cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int cu = cache[dev].load(std::memory_order_relaxed);
+    if (cu == 0) {
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
             cu = 256;
-        heads = 4L * cu;
-        cache[dev].store(heads, std::memory_order_relaxed);
+        cache[dev].store(cu, std::memory_order_relaxed);
     }
-    return heads;
+    return cu;
 }
+
+// Heads that one round of the single-token 128 x 128 kernel holds at two
+// wavefronts per head and two wavefronts per SIMD: four per compute unit.
+static long resident_heads() { return 4L * cu_count(); }
 
 // Column blocks per head: a grid that would fill less than one resident
 // round (two wavefronts per SIMD) is split into 4 or 2 blocks of whole
