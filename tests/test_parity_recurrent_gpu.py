@@ -182,9 +182,10 @@ def test_repeat_runs_bitwise_deterministic():
         assert np.array_equal(a, b)
 
 
-def test_rollback_edge_cases_and_error_flag():
+@pytest.mark.parametrize("d", [64, 128])  # 128: few 64 KiB tiles, each copied by four workgroups
+def test_rollback_edge_cases_and_error_flag(d):
     rng = np.random.default_rng(8)
-    B, H, K, d = 6, 3, 4, 64
+    B, H, K = 6, 3, 4
     st_np = rng.standard_normal((B, H, K, d, d)).astype(np.float32)
     st = torch.from_numpy(st_np.copy()).to("cuda")
     acc_np = np.array([0, 3, -1, 4, 1, 2], dtype=np.int32)
