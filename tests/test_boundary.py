@@ -387,3 +387,15 @@ def test_bench_traffic_tied_to_kernel_sources(monkeypatch):
     assert got == pytest.approx(want, rel=1e-12)
     algorithmic = bench.recurrent_bytes(64, 1, 16, 128, 1, False, True)
     assert 0.9 < got / algorithmic < 1.3
+
+
+def test_bench_decode_traffic_matches_kernel_sources():
+    """bench.py reports the decode kernel's counter-measured HBM traffic only
+    while the kernel sources are those the counters were taken on; the
+    committed figures must describe the committed sources."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    nbytes = bench.decode_traffic_bytes()
+    assert nbytes is not None, "decode traffic counters describe other kernel sources: collect them again"
+    assert 1.0 <= nbytes / 135536640 < 1.05  # within 5% above the algorithmic bytes
