@@ -71,7 +71,7 @@ def test_speculative_rounds_match_oracle(path, B, T, H, d, K, gate, tol):
             assert e <= tol, (r, name, e)
         assert int(err.item()) == (1 if n_bad else 0), r
         ref = rst
-        # the next round's accepted lengths; round 2 carries one invalid entry
+        # the next accepted lengths; those verified in the third speculative round include an invalid one
         acc = rng.integers(0, min(T, K - 1) + 1, size=B).astype(np.int32)
         if r == 1:
             acc[-1] = K + 3
