@@ -1553,7 +1553,24 @@ prefill_chain_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int a = 0; a < A; ++a)
             if (a < NC)
                 for (int qt = 0; qt < 3; ++qt) load(a, qt);
-        vm_wait_all();
+        // chunk 0's loads are done; those of chunks 1 and 2 may stay
+        // outstanding (each is waited for at the end of the chunk before it).
+        // Measured against waiting for all three: 128 tokens of 16 heads
+        // 12.8 us against 13.0, 1024 tokens 32.3 against 33.0
+        static_assert(A == 3, "the start-up waits count three chunks");
+        if (NC >= 3) {
+            if (l < kLoadWaves - 1)
+                vm_wait_keep<2 * kPer>();
+            else
+                vm_wait_keep<2 * kLast>();
+        } else if (NC == 2) {
+            if (l < kLoadWaves - 1)
+                vm_wait_keep<kPer>();
+            else
+                vm_wait_keep<kLast>();
+        } else {
+            vm_wait_all();
+        }
         for (int n = 0; n < NC; ++n) {
             const bool more = n + A < NC;  // slot (n + A) % kRing was last read before B1
             lds_barrier();  // B1
