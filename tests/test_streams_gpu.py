@@ -1,4 +1,5 @@
-"""Concurrent calls on separate streams and host threads.
+"""Concurrent calls on separate streams and host threads, and an aliased
+output refused through the binding.
 
 The library keeps no state between calls apart from a per-device compute-unit
 count (and the allocation-free prefill's fixed scratch array, which is not
@@ -115,3 +116,18 @@ def test_concurrent_streams_and_threads_match_sequential():
         for rep, outs in enumerate(results[i]):
             for j, (a, b) in enumerate(zip(outs, r)):
                 assert np.array_equal(a, b), (i, rep, j)
+
+
+def test_overlapping_output_raises_before_any_launch():
+    """A final state that is a view of the state's own memory is refused with
+    GDN_ERR_ALIAS (raised as GdnError) and nothing is written."""
+    import linear_attention_recurrence_net_amd as gdn
+    c = gi.make_case(2, 3, 2, 64, K=4, gate="gda", qkv_dtype="bf16", seed=3010)
+    u = upload(c)
+    st = u["state"]
+    before = bits(st)
+    fin = st.view(-1)[: 2 * 2 * 64 * 64].view(2, 2, 64, 64)  # slot 0 of the first heads
+    with pytest.raises(gdn.GdnError, match="overlaps"):
+        gdn.gdn_forward_snapshots(u["q"], u["k"], u["v"], u["g"], u["beta"], st, fin)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(st), before)
